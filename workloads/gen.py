@@ -1,0 +1,283 @@
+"""Seeded workload generators.
+
+Every random draw comes from ``numpy.random.default_rng(SeedSequence([wid,
+stream, ...]))`` where ``wid`` identifies the workload and ``stream`` the kind
+of draw:
+
+    0  document contents (per document id)
+    1  document choice and order (per request)
+    2  suffix (question) q/k/v (per request)
+    3  decode-step q/k/v (per step)
+    4  lengths (mixed-batch decode context sizes)
+
+so any single document, request or step can be regenerated on its own.  Draws
+are fp32 normals; bf16 workloads round them to the nearest bf16 (ties to even)
+once, here, and both sides consume the rounded values.
+
+Nothing in this module implements the method's arithmetic (no rotation, no
+attention, no packing).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+BLOCK_SIZE = 16
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returns fp32 holding bf16-exact values."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    bias = np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
+    r = ((u + bias) & np.uint64(0xFFFF0000)).astype(np.uint32)
+    return r.view(np.float32)
+
+
+@dataclass(frozen=True)
+class Geometry:
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str  # "fp32" or "bf16"
+    block_size: int = BLOCK_SIZE
+
+
+@dataclass(frozen=True)
+class PosSpec:
+    """Positional-encoding variant parameters (no derived quantities)."""
+
+    kind: str  # "rope_half", "rope_interleaved" or "alibi"
+    base: float = 10000.0
+    yarn_factor: float = 1.0  # 1.0 = plain RoPE
+    yarn_orig_ctx: int = 0
+    yarn_beta_fast: float = 32.0
+    yarn_beta_slow: float = 1.0
+
+
+@dataclass
+class PrefillRequest:
+    doc_ids: List[int]
+    q: np.ndarray  # [Lq][Hq][dh] raw (pre-position) question queries
+    k: np.ndarray  # [Lq][Hkv][dh]
+    v: np.ndarray  # [Lq][Hkv][dh]
+
+
+@dataclass
+class DecodeRequest:
+    doc_ids: List[int]
+    # question tokens that precede generation (may be empty: Lq = 0)
+    k: np.ndarray  # [Lq][Hkv][dh]
+    v: np.ndarray  # [Lq][Hkv][dh]
+
+
+@dataclass
+class Workload:
+    name: str
+    wid: int
+    geom: Geometry
+    pos: PosSpec
+    kv_scale: float
+    doc_lens: Dict[int, int]
+    prefill_steps: List[List[PrefillRequest]] = field(default_factory=list)
+    decode_reqs: List[DecodeRequest] = field(default_factory=list)
+    num_decode_steps: int = 0
+    description: str = ""
+    kv_budget_blocks: Optional[int] = None  # document-cache budget in blocks (None = unlimited)
+    _doc_cache: Dict[int, Tuple[np.ndarray, np.ndarray]] = field(default_factory=dict, repr=False)
+
+    # ----------------------------------------------------------------- draws
+    def _normal(self, seed: List[int], shape, scale: float) -> np.ndarray:
+        rng = np.random.default_rng(np.random.SeedSequence([self.wid] + list(seed)))
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        if scale != 1.0:
+            x *= np.float32(scale)
+        if self.geom.dtype == "bf16":
+            x = round_to_bf16(x)
+        return x
+
+    def doc(self, doc_id: int, cache: bool = True) -> Tuple[np.ndarray, np.ndarray]:
+        """Raw (content-only) k, v of one document: two fp32 arrays [L][Hkv][dh]."""
+        if doc_id in self._doc_cache:
+            return self._doc_cache[doc_id]
+        g = self.geom
+        L = self.doc_lens[doc_id]
+        both = self._normal([0, doc_id], (2, L, g.num_kv_heads, g.head_dim), self.kv_scale)
+        kv = (both[0], both[1])
+        if cache:
+            self._doc_cache[doc_id] = kv
+        return kv
+
+    def decode_step(self, step: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """q [R][Hq][dh], k [R][Hkv][dh], v [R][Hkv][dh] raw draws for every decode request at one step."""
+        g = self.geom
+        R = len(self.decode_reqs)
+        rng = np.random.default_rng(np.random.SeedSequence([self.wid, 3, step]))
+        q = rng.standard_normal(size=(R, g.num_q_heads, g.head_dim), dtype=np.float32)
+        kv = rng.standard_normal(size=(2, R, g.num_kv_heads, g.head_dim), dtype=np.float32)
+        kv *= np.float32(self.kv_scale)
+        if g.dtype == "bf16":
+            q, kv = round_to_bf16(q), round_to_bf16(kv)
+        return q, kv[0], kv[1]
+
+    # ------------------------------------------------------------ structure
+    def decode_ctx_len(self, r: int) -> int:
+        """Tokens before the first generated token of decode request r (documents + question)."""
+        req = self.decode_reqs[r]
+        return sum(self.doc_lens[d] for d in req.doc_ids) + req.k.shape[0]
+
+    def all_doc_ids(self) -> List[int]:
+        ids = set()
+        for step in self.prefill_steps:
+            for req in step:
+                ids.update(req.doc_ids)
+        for req in self.decode_reqs:
+            ids.update(req.doc_ids)
+        return sorted(ids)
+
+
+def _zipf_pick(wid: int, req_key: List[int], pool: int, n: int, alpha: float) -> List[int]:
+    """n distinct documents from a pool, Zipf(alpha) popularity by id rank, in a random order."""
+    rng = np.random.default_rng(np.random.SeedSequence([wid, 1] + list(req_key)))
+    w = np.arange(1, pool + 1, dtype=np.float64) ** (-alpha)
+    ids = rng.choice(pool, size=n, replace=False, p=w / w.sum())
+    return [int(i) for i in rng.permutation(ids)]
+
+
+def _question(wl: Workload, req_key: List[int], Lq: int, with_q: bool):
+    g = wl.geom
+    rng = np.random.default_rng(np.random.SeedSequence([wl.wid, 2] + list(req_key)))
+    q = rng.standard_normal(size=(Lq, g.num_q_heads, g.head_dim), dtype=np.float32)
+    kv = rng.standard_normal(size=(2, Lq, g.num_kv_heads, g.head_dim), dtype=np.float32)
+    kv *= np.float32(wl.kv_scale)
+    if g.dtype == "bf16":
+        q, kv = round_to_bf16(q), round_to_bf16(kv)
+    if with_q:
+        return PrefillRequest(doc_ids=[], q=q, k=kv[0], v=kv[1])
+    return DecodeRequest(doc_ids=[], k=kv[0], v=kv[1])
+
+
+# --------------------------------------------------------------------------- workloads
+
+def _tiny_fp32() -> Workload:
+    wl = Workload(
+        name="tiny_fp32_2doc_h4kv1_d64",
+        wid=1,
+        geom=Geometry(4, 1, 64, "fp32"),
+        pos=PosSpec("rope_half", base=1e4),
+        kv_scale=1.0,
+        doc_lens={0: 64, 1: 48},
+        num_decode_steps=8,
+        description="doc A (64 tok) || doc B (48 tok) || 16-token suffix, then 8 decode steps; fp32",
+    )
+    pre = _question(wl, [0], 16, True)
+    pre.doc_ids = [0, 1]
+    wl.prefill_steps = [[pre]]
+    # the decode request continues the same sequence: documents + the 16 suffix tokens
+    wl.decode_reqs = [DecodeRequest(doc_ids=[0, 1], k=pre.k, v=pre.v)]
+    return wl
+
+
+def _prefill_llama8b(kind: str, wid: int, name: str) -> Workload:
+    wl = Workload(
+        name=name,
+        wid=wid,
+        geom=Geometry(32, 8, 128, "bf16"),
+        pos=PosSpec(kind, base=5e5),
+        kv_scale=0.5,
+        doc_lens={d: 200 for d in range(100)},
+        description="8 requests x (10 Zipf(2.1) docs of 200 tok from a 100-doc pool + 32-tok question)",
+    )
+    reqs = []
+    for r in range(8):
+        pr = _question(wl, [r], 32, True)
+        pr.doc_ids = _zipf_pick(wid, [r], 100, 10, 2.1)
+        reqs.append(pr)
+    wl.prefill_steps = [reqs]
+    return wl
+
+
+def _decode_llama8b() -> Workload:
+    wl = Workload(
+        name="llama8b_decode_b64_ctx32k",
+        wid=3,
+        geom=Geometry(32, 8, 128, "bf16"),
+        pos=PosSpec("rope_half", base=5e5),
+        kv_scale=0.5,
+        doc_lens={d: 1600 for d in range(200)},
+        num_decode_steps=64,
+        description="64 requests x 20 Zipf(1.2) docs of 1600 tok (200-doc pool); 64 decode steps",
+    )
+    z = np.zeros((0, 8, 128), np.float32)
+    wl.decode_reqs = [DecodeRequest(doc_ids=_zipf_pick(3, [r], 200, 20, 1.2), k=z, v=z) for r in range(64)]
+    return wl
+
+
+def _mixed_llama70b(num_steps: int = 16) -> Workload:
+    wl = Workload(
+        name="llama70b_mixed_yarn8_p4x7.5k_d48x8k-64k",
+        wid=4,
+        geom=Geometry(64, 8, 128, "bf16"),
+        pos=PosSpec("rope_half", base=5e5, yarn_factor=8.0, yarn_orig_ctx=8192),
+        kv_scale=0.5,
+        doc_lens={d: 500 for d in range(1000)},
+        num_decode_steps=num_steps,
+        kv_budget_blocks=16384,
+        description=(
+            "per step: 4 prefills (15 Zipf(2.1) docs x 500 tok + 64-tok question) + 48 decodes "
+            "(n x 500-tok docs + 64-tok question, n ~ U{16..131}); 1000-doc pool; 1 GiB KV budget"
+        ),
+    )
+    rng = np.random.default_rng(np.random.SeedSequence([4, 4]))
+    ns = rng.integers(16, 132, size=48)
+    decs = []
+    for r in range(48):
+        dr = _question(wl, [1000 + r], 64, False)
+        dr.doc_ids = _zipf_pick(4, [1000 + r], 1000, int(ns[r]), 2.1)
+        decs.append(dr)
+    wl.decode_reqs = decs
+    steps = []
+    for s in range(num_steps):
+        reqs = []
+        for j in range(4):
+            pr = _question(wl, [s, j], 64, True)
+            pr.doc_ids = _zipf_pick(4, [s, j], 1000, 15, 2.1)
+            reqs.append(pr)
+        steps.append(reqs)
+    wl.prefill_steps = steps
+    return wl
+
+
+def _falcon_alibi() -> Workload:
+    wl = Workload(
+        name="falcon7b_mqa_alibi_b128_ctx16k",
+        wid=5,
+        geom=Geometry(71, 1, 64, "bf16"),
+        pos=PosSpec("alibi"),
+        kv_scale=0.5,
+        doc_lens={d: 2048 for d in range(64)},
+        num_decode_steps=64,
+        description="128 requests x 8 Zipf(1.5) docs of 2048 tok (64-doc pool); MQA 71 heads; 64 decode steps",
+    )
+    z = np.zeros((0, 1, 64), np.float32)
+    wl.decode_reqs = [DecodeRequest(doc_ids=_zipf_pick(5, [r], 64, 8, 1.5), k=z, v=z) for r in range(128)]
+    return wl
+
+
+WORKLOADS = {
+    "tiny_fp32": _tiny_fp32,
+    "llama8b_prefill": lambda: _prefill_llama8b("rope_half", 2, "llama8b_prefill_b8_10x200"),
+    "llama8b_decode": _decode_llama8b,
+    "llama70b_mixed": _mixed_llama70b,
+    "falcon7b_alibi": _falcon_alibi,
+    "llama8b_prefill_interleaved": lambda: _prefill_llama8b(
+        "rope_interleaved", 2, "llama8b_prefill_b8_10x200_interleaved"
+    ),
+}
+
+
+def make_workload(key: str, **kw) -> Workload:
+    return WORKLOADS[key](**kw)
