@@ -1,0 +1,215 @@
+// Host-side part of liblazyattn: error text, argument validation, the
+// positional-encoding metadata (RoPE / YaRN frequencies, cos/sin table, ALiBi
+// slopes) and the tile-word packer / per-request tile builder.  Pure host
+// code; nothing here touches the GPU.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "lazy_host.hpp"
+
+namespace lazy {
+
+static thread_local std::string g_err;
+
+lazy_status fail(lazy_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+void clear_error() { g_err.clear(); }
+
+lazy_status check_geom(const lazy_geom* g) {
+  if (!g) return fail(LAZY_ERR_ARG, "geom is NULL");
+  if (g->num_kv_heads < 1 || g->num_q_heads < 1)
+    return fail(LAZY_ERR_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", g->num_q_heads, g->num_kv_heads);
+  if (g->num_q_heads % g->num_kv_heads != 0)
+    return fail(LAZY_ERR_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", g->num_q_heads,
+                g->num_kv_heads);
+  if (g->num_q_heads / g->num_kv_heads > 128)
+    return fail(LAZY_ERR_UNSUPPORTED, "more than 128 query heads per KV head");
+  if (g->head_dim != 64 && g->head_dim != 128)
+    return fail(LAZY_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", g->head_dim);
+  if (g->block_size != LAZY_BLOCK_SIZE)
+    return fail(LAZY_ERR_UNSUPPORTED, "block_size must be %d (got %d)", LAZY_BLOCK_SIZE, g->block_size);
+  if (g->dtype != LAZY_BF16 && g->dtype != LAZY_FP32) return fail(LAZY_ERR_ARG, "unknown dtype %d", g->dtype);
+  return LAZY_OK;
+}
+
+lazy_status check_pos(const lazy_geom* g, const lazy_pos_desc* p) {
+  if (!p) return fail(LAZY_ERR_ARG, "pos descriptor is NULL");
+  if (p->kind != LAZY_ROPE_HALF && p->kind != LAZY_ROPE_INTERLEAVED && p->kind != LAZY_ALIBI)
+    return fail(LAZY_ERR_ARG, "unknown positional kind %d", p->kind);
+  if (p->flags & ~LAZY_FLAG_PREROTATED) return fail(LAZY_ERR_ARG, "unknown flags 0x%x", p->flags);
+  if (!(p->softmax_scale > 0.f) || !isfinite(p->softmax_scale))
+    return fail(LAZY_ERR_ARG, "softmax_scale must be finite and > 0");
+  if (p->kind == LAZY_ALIBI) {
+    if (!p->alibi_slopes) return fail(LAZY_ERR_ARG, "ALiBi needs alibi_slopes");
+    (void)g;
+    return LAZY_OK;
+  }
+  if (p->cos_sin) {
+    if (p->max_pos < 1) return fail(LAZY_ERR_ARG, "max_pos must be >= 1 with a cos/sin table");
+  } else if (!p->inv_freq) {
+    return fail(LAZY_ERR_ARG, "RoPE needs cos_sin or inv_freq");
+  }
+  return LAZY_OK;
+}
+
+}  // namespace lazy
+
+using namespace lazy;
+
+extern "C" const char* lazy_last_error(void) { return g_err.c_str(); }
+
+extern "C" lazy_status lazy_rope_freqs(int32_t head_dim, double base, double yarn_factor, int32_t yarn_orig_ctx,
+                                       double beta_fast, double beta_slow, double* inv_freq_out,
+                                       double* logit_gain) {
+  clear_error();
+  if (head_dim < 2 || head_dim % 2) return fail(LAZY_ERR_ARG, "head_dim must be even and >= 2");
+  if (!(base > 1.0)) return fail(LAZY_ERR_ARG, "base must be > 1");
+  if (!inv_freq_out) return fail(LAZY_ERR_ARG, "inv_freq_out is NULL");
+  const bool yarn = yarn_factor > 1.0;
+  if (yarn && (yarn_orig_ctx < 1 || !(beta_fast > beta_slow)))
+    return fail(LAZY_ERR_ARG, "YaRN needs orig_ctx >= 1 and beta_fast > beta_slow");
+  const int half = head_dim / 2;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int k = 0; k < half; ++k) {
+    // textbook RoPE frequency base^(-2k/dh)
+    const double theta = pow(base, -(double)(2 * k) / (double)head_dim);
+    double f = theta;
+    if (yarn) {
+      // YaRN "NTK-by-parts": r = rotations of this pair over the original
+      // context; linear ramp between beta_slow and beta_fast rotations blends
+      // interpolation (theta / s) with extrapolation (theta).
+      const double r = (double)yarn_orig_ctx * theta / two_pi;
+      double gamma = (r - beta_slow) / (beta_fast - beta_slow);
+      gamma = gamma < 0.0 ? 0.0 : (gamma > 1.0 ? 1.0 : gamma);
+      f = (1.0 - gamma) * theta / yarn_factor + gamma * theta;
+    }
+    inv_freq_out[k] = f;
+  }
+  if (logit_gain) {
+    const double t = yarn ? 0.1 * log(yarn_factor) + 1.0 : 1.0;
+    *logit_gain = t * t;
+  }
+  return LAZY_OK;
+}
+
+extern "C" lazy_status lazy_rope_table(int32_t head_dim, const double* inv_freq, int32_t max_pos, float* table_out) {
+  clear_error();
+  if (head_dim < 2 || head_dim % 2) return fail(LAZY_ERR_ARG, "head_dim must be even and >= 2");
+  if (max_pos < 1) return fail(LAZY_ERR_ARG, "max_pos must be >= 1");
+  if (!inv_freq || !table_out) return fail(LAZY_ERR_ARG, "NULL pointer");
+  const int half = head_dim / 2;
+  for (int64_t p = 0; p < max_pos; ++p) {
+    float* row = table_out + p * head_dim;
+    for (int k = 0; k < half; ++k) {
+      const double phi = (double)p * inv_freq[k];
+      row[k] = (float)cos(phi);
+      row[half + k] = (float)sin(phi);
+    }
+  }
+  return LAZY_OK;
+}
+
+extern "C" lazy_status lazy_alibi_slopes(int32_t num_heads, float* slopes_out) {
+  clear_error();
+  if (num_heads < 1 || !slopes_out) return fail(LAZY_ERR_ARG, "num_heads must be >= 1 and slopes_out non-NULL");
+  for (int h = 0; h < num_heads; ++h) slopes_out[h] = (float)exp2(-8.0 * (double)(h + 1) / (double)num_heads);
+  return LAZY_OK;
+}
+
+extern "C" lazy_status lazy_pack_tiles(const int64_t* block_ids, const int64_t* offsets, const uint32_t* masks,
+                                       int64_t n, uint64_t* out_words) {
+  clear_error();
+  if (n < 0) return fail(LAZY_ERR_ARG, "n must be >= 0");
+  if (n > 0 && (!block_ids || !offsets || !masks || !out_words)) return fail(LAZY_ERR_ARG, "NULL pointer");
+  for (int64_t i = 0; i < n; ++i) {
+    if (block_ids[i] < 0 || block_ids[i] > LAZY_MAX_BLOCK_ID)
+      return fail(LAZY_ERR_ARG, "tile %lld: block id %lld outside [0, 2^24)", (long long)i, (long long)block_ids[i]);
+    if (offsets[i] < 0 || offsets[i] > LAZY_MAX_OFFSET)
+      return fail(LAZY_ERR_ARG, "tile %lld: offset %lld outside [0, 2^24)", (long long)i, (long long)offsets[i]);
+    if (masks[i] == 0 || masks[i] > 0xFFFFu)
+      return fail(LAZY_ERR_ARG, "tile %lld: mask 0x%x outside [1, 0xFFFF]", (long long)i, masks[i]);
+    out_words[i] = ((uint64_t)block_ids[i] << 40) | ((uint64_t)offsets[i] << 16) | (uint64_t)masks[i];
+  }
+  return LAZY_OK;
+}
+
+extern "C" lazy_status lazy_unpack_tiles(const uint64_t* words, int64_t n, int64_t* block_ids, int64_t* offsets,
+                                         uint32_t* masks) {
+  clear_error();
+  if (n < 0) return fail(LAZY_ERR_ARG, "n must be >= 0");
+  if (n > 0 && !words) return fail(LAZY_ERR_ARG, "NULL words");
+  for (int64_t i = 0; i < n; ++i) {
+    const uint64_t w = words[i];
+    if (block_ids) block_ids[i] = (int64_t)(w >> 40);
+    if (offsets) offsets[i] = (int64_t)((w >> 16) & 0xFFFFFFull);
+    if (masks) masks[i] = (uint32_t)(w & 0xFFFFull);
+  }
+  return LAZY_OK;
+}
+
+extern "C" lazy_status lazy_build_tiles(int32_t kind, int32_t num_reqs, const int32_t* seg_start,
+                                        const int32_t* seg_len, const int64_t* seg_pos0, const uint8_t* seg_is_ctx,
+                                        const int32_t* seg_block_start, const int32_t* blocks, int64_t num_blocks,
+                                        uint64_t* tiles_out, int64_t tiles_cap, int32_t* tile_start,
+                                        int32_t* ctx_tiles) {
+  clear_error();
+  if (kind != LAZY_ROPE_HALF && kind != LAZY_ROPE_INTERLEAVED && kind != LAZY_ALIBI)
+    return fail(LAZY_ERR_ARG, "unknown positional kind %d", kind);
+  if (num_reqs < 0) return fail(LAZY_ERR_ARG, "num_reqs must be >= 0");
+  if (!seg_start || !tile_start || !ctx_tiles) return fail(LAZY_ERR_ARG, "NULL pointer");
+  if (seg_start[0] != 0) return fail(LAZY_ERR_ARG, "seg_start[0] must be 0");
+  const int32_t nseg = seg_start[num_reqs];
+  if (nseg > 0 && (!seg_len || !seg_pos0 || !seg_is_ctx || !seg_block_start || !blocks))
+    return fail(LAZY_ERR_ARG, "NULL segment array");
+  if (num_blocks < 1 || num_blocks > (int64_t)LAZY_MAX_BLOCK_ID + 1)
+    return fail(LAZY_ERR_ARG, "num_blocks must be in [1, 2^24]");
+  int64_t nt = 0;
+  for (int r = 0; r < num_reqs; ++r) {
+    if (seg_start[r + 1] < seg_start[r]) return fail(LAZY_ERR_ARG, "seg_start decreases at request %d", r);
+    if (nt > INT32_MAX) return fail(LAZY_ERR_ARG, "too many tiles");
+    tile_start[r] = (int32_t)nt;
+    int32_t nctx = 0;
+    bool seen_private = false;
+    for (int s = seg_start[r]; s < seg_start[r + 1]; ++s) {
+      const int32_t L = seg_len[s];
+      const int64_t p0 = seg_pos0[s];
+      const bool ctx = seg_is_ctx[s] != 0;
+      if (L < 0) return fail(LAZY_ERR_ARG, "segment %d: negative length", s);
+      if (p0 < 0) return fail(LAZY_ERR_ARG, "segment %d: negative position", s);
+      if (ctx && seen_private) return fail(LAZY_ERR_ARG, "request %d: context segment %d after a private one", r, s);
+      if (!ctx) seen_private = true;
+      const int32_t nblk = (L + LAZY_BLOCK_SIZE - 1) / LAZY_BLOCK_SIZE;
+      if (seg_block_start[s + 1] - seg_block_start[s] < nblk)
+        return fail(LAZY_ERR_ARG, "segment %d: %d blocks for %d tokens", s, seg_block_start[s + 1] - seg_block_start[s],
+                    L);
+      for (int32_t b = 0; b < nblk; ++b) {
+        const int64_t blk = blocks[seg_block_start[s] + b];
+        const int32_t valid = (L - LAZY_BLOCK_SIZE * b) < LAZY_BLOCK_SIZE ? (L - LAZY_BLOCK_SIZE * b) : LAZY_BLOCK_SIZE;
+        const uint32_t mask = (uint32_t)((1u << valid) - 1u);
+        // rotary context tile: the document's start (the rotation amount);
+        // otherwise the global position of the tile's first slot
+        const int64_t off = (ctx && kind != LAZY_ALIBI) ? p0 : p0 + (int64_t)LAZY_BLOCK_SIZE * b;
+        if (blk < 0 || blk >= num_blocks)
+          return fail(LAZY_ERR_ARG, "segment %d block %d: id %lld outside the pool", s, b, (long long)blk);
+        if (off > LAZY_MAX_OFFSET) return fail(LAZY_ERR_ARG, "segment %d: offset %lld exceeds 2^24-1", s, (long long)off);
+        if (nt >= tiles_cap) return fail(LAZY_ERR_ARG, "tiles_cap %lld too small", (long long)tiles_cap);
+        tiles_out[nt++] = ((uint64_t)blk << 40) | ((uint64_t)off << 16) | (uint64_t)mask;
+        if (ctx) ++nctx;
+      }
+    }
+    ctx_tiles[r] = nctx;
+  }
+  tile_start[num_reqs] = (int32_t)nt;
+  return LAZY_OK;
+}

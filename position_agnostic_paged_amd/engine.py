@@ -1,0 +1,150 @@
+"""Device state and call sequencing for the deferred-position paged attention path.
+
+``PosDesc`` builds the positional metadata once (host C calls for the
+frequencies / cos-sin table / ALiBi slopes, then a copy to the device).
+``Engine`` owns the paged K/V pools and runs the three device calls of the
+library: kv-write (documents at local positions, private tokens at global
+positions), prefill and decode, with tile tables built by the library's host
+packer.  PyTorch provides device memory, copies and the stream; every step of
+the computation runs in liblazyattn.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import lazy_attn as L
+from .paging import BlockPool, DocCache, RequestLayout, blocks_for, flatten_layouts
+
+TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+class PosDesc:
+    """Positional variant: kind, softmax scale and device-resident coefficients."""
+
+    def __init__(self, kind: str, head_dim: int, num_q_heads: int, device, base: float = 1e4,
+                 yarn_factor: float = 1.0, yarn_orig_ctx: int = 0, beta_fast: float = 32.0, beta_slow: float = 1.0,
+                 max_pos: int = 0, on_the_fly: bool = False, prerotated: bool = False):
+        self.kind = kind
+        self.kind_id = L.KIND_BY_NAME[kind]
+        self.head_dim = head_dim
+        self.table = self.inv_freq = self.slopes = None
+        gain = 1.0
+        if kind == "alibi":
+            self.slopes = torch.from_numpy(L.alibi_slopes(num_q_heads)).to(device)
+            max_pos = max(max_pos, 1)
+        else:
+            inv, gain = L.rope_freqs(head_dim, base, yarn_factor, yarn_orig_ctx, beta_fast, beta_slow)
+            self.inv_freq = torch.from_numpy(inv).to(device)
+            if not on_the_fly:
+                if max_pos < 1:
+                    raise ValueError("max_pos must cover every rotation position")
+                self.table = torch.from_numpy(L.rope_table(head_dim, inv, max_pos)).to(device)
+        self.max_pos = max_pos
+        self.softmax_scale = gain / math.sqrt(head_dim)
+        self.c = L.PosDescC(self.kind_id, L.LAZY_FLAG_PREROTATED if prerotated else 0, max_pos,
+                            self.softmax_scale, L._dev(self.table), L._dev(self.inv_freq), L._dev(self.slopes))
+
+    def with_flags(self, prerotated: bool) -> L.PosDescC:
+        c = L.PosDescC.from_buffer_copy(self.c)
+        c.flags = L.LAZY_FLAG_PREROTATED if prerotated else 0
+        return c
+
+
+class TileTable:
+    """Device copy of the packed tile words of a batch of requests."""
+
+    def __init__(self, layouts: Sequence[RequestLayout], kind_id: int, num_blocks: int, device):
+        f = flatten_layouts(layouts)
+        cap = sum(blocks_for(n) for n in f["seg_len"]) or 1
+        tiles, tstart, nctx = L.build_tiles(kind_id, f["seg_start"], f["seg_len"], f["seg_pos0"], f["seg_is_ctx"],
+                                            f["seg_block_start"], f["blocks"] or [0], num_blocks, cap)
+        self.host_tiles, self.host_start, self.host_ctx = tiles, tstart, nctx
+        self.num_reqs = len(layouts)
+        self.max_tiles = int(np.max(np.diff(tstart))) if len(layouts) else 0
+        self.tiles = torch.from_numpy(tiles.view(np.int64) if tiles.size else np.zeros(1, np.int64)).to(device)
+        self.tile_start = torch.from_numpy(tstart).to(device)
+        self.ctx_tiles = torch.from_numpy(nctx if nctx.size else np.zeros(1, np.int32)).to(device)
+
+
+class Engine:
+    def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str, pos: PosDesc,
+                 num_blocks: int, device="cuda", budget_blocks: Optional[int] = None):
+        self.geom = L.make_geom(num_q_heads, num_kv_heads, head_dim, dtype)
+        self.hq, self.hkv, self.dh, self.dtype = num_q_heads, num_kv_heads, head_dim, dtype
+        self.tdtype = TORCH_DTYPE[dtype]
+        self.pos = pos
+        self.device = torch.device(device)
+        self.num_blocks = num_blocks
+        self.k_cache = torch.empty((num_blocks, num_kv_heads, 16, head_dim), dtype=self.tdtype, device=self.device)
+        self.v_cache = torch.empty((num_blocks, num_kv_heads, head_dim, 16), dtype=self.tdtype, device=self.device)
+        self.pool = BlockPool(num_blocks)
+        self.docs = DocCache(self.pool, budget_blocks)
+        self._ws: Optional[torch.Tensor] = None
+
+    # ------------------------------------------------------------- writing
+    def kv_write(self, k: torch.Tensor, v: torch.Tensor, q: Optional[torch.Tensor], positions: torch.Tensor,
+                 slots: torch.Tensor, pos: Optional[L.PosDescC] = None, stream=None) -> None:
+        L.kv_write(self.geom, self.pos.c if pos is None else pos, self.k_cache, self.v_cache, self.num_blocks, k, v, q,
+                   positions, slots, stream)
+
+    def slots_for(self, blocks: Sequence[int], length: int, first: int = 0) -> np.ndarray:
+        """Slot ids of tokens first .. first+length-1 of a segment stored in ``blocks``."""
+        idx = np.arange(first, first + length)
+        b = np.asarray(blocks, np.int64)[idx // 16]
+        return b * 16 + idx % 16
+
+    def write_segment(self, blocks: Sequence[int], k: torch.Tensor, v: torch.Tensor, pos0: int,
+                      q: Optional[torch.Tensor] = None, first: int = 0, stream=None) -> None:
+        """Write tokens first.. of a segment; their rotation positions are pos0 + first + i.
+
+        For a cached document pos0 = 0 (local positions: the position-agnostic
+        copy); for private tokens pos0 is the segment's global start."""
+        n = k.shape[0]
+        if n == 0:
+            return
+        positions = torch.arange(pos0 + first, pos0 + first + n, dtype=torch.int32).to(self.device)
+        slots = torch.from_numpy(self.slots_for(blocks, n, first)).to(self.device)
+        self.kv_write(k, v, q, positions, slots, stream=stream)
+
+    def cache_doc(self, doc_id: int, length: int, content_fn, reserve: int = 0) -> Tuple[List[int], bool]:
+        """Pin a document, writing its position-agnostic copy on a miss.  content_fn() -> (k, v) device tensors."""
+        blocks, hit = self.docs.acquire(doc_id, length, reserve)
+        if not hit:
+            k, v = content_fn()
+            self.write_segment(blocks, k, v, 0)
+        return blocks, hit
+
+    # ----------------------------------------------------------- attention
+    def _workspace(self, nbytes: int) -> Optional[torch.Tensor]:
+        if nbytes == 0:
+            return None
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def tile_table(self, layouts: Sequence[RequestLayout]) -> TileTable:
+        return TileTable(layouts, self.pos.kind_id, self.num_blocks, self.device)
+
+    def prefill(self, tt: TileTable, q: torch.Tensor, q_start: torch.Tensor, q_pos0: torch.Tensor, max_q_len: int,
+                out: Optional[torch.Tensor] = None, pos: Optional[L.PosDescC] = None, stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self._workspace(L.workspace_size(self.geom, tt.num_reqs, max_q_len, tt.max_tiles, True))
+        L.attn_prefill(self.geom, self.pos.c if pos is None else pos, self.k_cache, self.v_cache, self.num_blocks,
+                       tt.tiles, tt.tile_start, tt.ctx_tiles, q, q_start, q_pos0, tt.num_reqs, max_q_len, tt.max_tiles,
+                       out, ws, stream)
+        return out
+
+    def decode(self, tt: TileTable, q: torch.Tensor, q_pos: torch.Tensor, out: Optional[torch.Tensor] = None,
+               pos: Optional[L.PosDescC] = None, stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self._workspace(L.workspace_size(self.geom, tt.num_reqs, 1, tt.max_tiles, False))
+        L.attn_decode(self.geom, self.pos.c if pos is None else pos, self.k_cache, self.v_cache, self.num_blocks,
+                      tt.tiles, tt.tile_start, tt.ctx_tiles, q, q_pos, tt.num_reqs, tt.max_tiles, out, ws, stream)
+        return out

@@ -1,0 +1,188 @@
+"""Host-side paging: a block pool, a position-agnostic document cache and
+request layouts.  Pure Python, no device work.
+
+One cached copy per document, reused at any position (LazyAttention notes,
+papernotes.org, "Background and motivation": a position-agnostic cache keeps
+the top-C documents instead of floor(C/D) position variants; repository
+landing page, "Demo": one copy per document reused regardless of slot).
+Documents are cached whole and evicted whole in least-recently-used order;
+documents referenced by the work in flight are pinned.
+"""
+
+from __future__ import annotations
+
+from collections import OrderedDict
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+BLOCK_SIZE = 16
+
+
+def blocks_for(tokens: int) -> int:
+    return (tokens + BLOCK_SIZE - 1) // BLOCK_SIZE
+
+
+class CacheFull(RuntimeError):
+    pass
+
+
+class BlockPool:
+    """Free list of physical block ids [0, num_blocks)."""
+
+    def __init__(self, num_blocks: int):
+        self.num_blocks = num_blocks
+        self._free: List[int] = list(range(num_blocks - 1, -1, -1))
+
+    @property
+    def free_blocks(self) -> int:
+        return len(self._free)
+
+    def alloc(self, n: int) -> List[int]:
+        if n > len(self._free):
+            raise CacheFull(f"need {n} blocks, {len(self._free)} free")
+        out = [self._free.pop() for _ in range(n)]
+        return out
+
+    def free(self, blocks: Sequence[int]) -> None:
+        self._free.extend(reversed(list(blocks)))
+
+
+@dataclass
+class CachedDoc:
+    blocks: List[int]
+    length: int
+    pins: int = 0
+
+
+class DocCache:
+    """doc id -> blocks of its position-agnostic copy, with LRU eviction of unpinned documents."""
+
+    def __init__(self, pool: BlockPool, budget_blocks: Optional[int] = None):
+        self.pool = pool
+        self.budget = budget_blocks if budget_blocks is not None else pool.num_blocks
+        self._docs: "OrderedDict[int, CachedDoc]" = OrderedDict()
+        self.used = 0
+        self.hits = 0
+        self.misses = 0
+        self.evictions = 0
+
+    def __contains__(self, doc_id: int) -> bool:
+        return doc_id in self._docs
+
+    def __len__(self) -> int:
+        return len(self._docs)
+
+    def blocks(self, doc_id: int) -> List[int]:
+        return self._docs[doc_id].blocks
+
+    def acquire(self, doc_id: int, length: int, reserve: int = 0) -> Tuple[List[int], bool]:
+        """Pin a document; returns (blocks, hit).  On a miss the caller must write its content.
+
+        ``reserve`` blocks of the budget are kept free for other allocations
+        (private suffix blocks come from the same budget).
+        """
+        d = self._docs.get(doc_id)
+        if d is not None:
+            if d.length != length:
+                raise ValueError(f"doc {doc_id} cached with length {d.length}, asked {length}")
+            self._docs.move_to_end(doc_id)
+            d.pins += 1
+            self.hits += 1
+            return d.blocks, True
+        need = blocks_for(length)
+        self._make_room(need + reserve)
+        blocks = self.pool.alloc(need)
+        self._docs[doc_id] = CachedDoc(blocks, length, pins=1)
+        self.used += need
+        self.misses += 1
+        return blocks, False
+
+    def release(self, doc_id: int) -> None:
+        d = self._docs[doc_id]
+        if d.pins <= 0:
+            raise ValueError(f"doc {doc_id} is not pinned")
+        d.pins -= 1
+
+    def _make_room(self, need: int) -> None:
+        def room() -> int:
+            return min(self.budget - self.used, self.pool.free_blocks)
+
+        if room() >= need:
+            return
+        for doc_id in list(self._docs.keys()):  # least recently used first
+            if room() >= need:
+                break
+            d = self._docs[doc_id]
+            if d.pins > 0:
+                continue
+            del self._docs[doc_id]
+            self.pool.free(d.blocks)
+            self.used -= len(d.blocks)
+            self.evictions += 1
+        if room() < need:
+            raise CacheFull(f"cannot free {need} blocks: everything left is pinned")
+
+    def room_for_private(self, n: int) -> bool:
+        """Whether n private blocks fit the budget after evicting every unpinned document."""
+        evictable = sum(len(d.blocks) for d in self._docs.values() if d.pins == 0)
+        return min(self.budget - self.used + evictable, self.pool.free_blocks + evictable) >= n
+
+    def take_private(self, n: int) -> List[int]:
+        """Blocks for private tokens, charged to the same budget (evicting if needed)."""
+        self._make_room(n)
+        self.used += n
+        return self.pool.alloc(n)
+
+    def give_back_private(self, blocks: Sequence[int]) -> None:
+        self.pool.free(blocks)
+        self.used -= len(blocks)
+
+
+@dataclass
+class Segment:
+    blocks: List[int]
+    length: int
+    pos0: int
+    ctx: bool  # True: cached document written at local positions; False: private, at global positions
+
+
+@dataclass
+class RequestLayout:
+    """A request's logical sequence: cached documents (in order), then private tokens."""
+
+    segments: List[Segment] = field(default_factory=list)
+
+    @property
+    def length(self) -> int:
+        return sum(s.length for s in self.segments)
+
+    @property
+    def num_tiles(self) -> int:
+        return sum(blocks_for(s.length) for s in self.segments)
+
+
+def layout_request(doc_blocks: Sequence[Tuple[List[int], int]], private_blocks: List[int],
+                   private_len: int) -> RequestLayout:
+    """Place documents consecutively from position 0, then the private tokens."""
+    segs = []
+    pos = 0
+    for blocks, length in doc_blocks:
+        segs.append(Segment(list(blocks), length, pos, True))
+        pos += length
+    segs.append(Segment(list(private_blocks), private_len, pos, False))
+    return RequestLayout(segs)
+
+
+def flatten_layouts(layouts: Sequence[RequestLayout]) -> Dict[str, list]:
+    """Segment arrays in the form lazy_build_tiles takes."""
+    seg_start, seg_len, seg_pos0, seg_ctx, seg_bstart, blocks = [0], [], [], [], [0], []
+    for lay in layouts:
+        for s in lay.segments:
+            seg_len.append(s.length)
+            seg_pos0.append(s.pos0)
+            seg_ctx.append(1 if s.ctx else 0)
+            blocks.extend(s.blocks)
+            seg_bstart.append(len(blocks))
+        seg_start.append(len(seg_len))
+    return {"seg_start": seg_start, "seg_len": seg_len, "seg_pos0": seg_pos0, "seg_is_ctx": seg_ctx,
+            "seg_block_start": seg_bstart, "blocks": blocks}

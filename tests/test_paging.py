@@ -1,0 +1,57 @@
+"""Host paging: block pool, document cache (one copy per document, LRU eviction of whole unpinned
+documents, private blocks charged to the same budget) and request layouts."""
+
+import pytest
+
+from position_agnostic_paged_amd.paging import BlockPool, CacheFull, DocCache, blocks_for, layout_request
+
+
+def test_blocks_for():
+    assert [blocks_for(n) for n in (0, 1, 16, 17, 200, 500, 1600)] == [0, 1, 1, 2, 13, 32, 100]
+
+
+def test_one_copy_per_document_and_hits():
+    c = DocCache(BlockPool(100))
+    b1, hit1 = c.acquire(7, 40)
+    b2, hit2 = c.acquire(7, 40)
+    assert not hit1 and hit2 and b1 == b2 and len(b1) == 3
+    assert c.used == 3 and c.hits == 1 and c.misses == 1
+
+
+def test_lru_evicts_least_recent_unpinned_whole_documents():
+    c = DocCache(BlockPool(10))
+    for d in range(3):  # 3 docs x 3 blocks
+        c.acquire(d, 48)
+        c.release(d)
+    c.acquire(0, 48)  # doc 0 becomes most recent (and pinned)
+    c.acquire(3, 48)  # needs 3 blocks, 1 free -> evict doc 1 (LRU, unpinned)
+    assert 1 not in c and 0 in c and 2 in c and 3 in c
+    assert c.evictions == 1
+
+
+def test_pinned_documents_are_never_evicted():
+    c = DocCache(BlockPool(6))
+    c.acquire(0, 48)
+    c.acquire(1, 48)
+    with pytest.raises(CacheFull):
+        c.acquire(2, 16)
+    c.release(1)
+    blocks, hit = c.acquire(2, 16)
+    assert not hit and 1 not in c and 0 in c
+
+
+def test_private_blocks_share_the_budget():
+    c = DocCache(BlockPool(100), budget_blocks=8)
+    c.acquire(0, 64)  # 4 blocks
+    c.release(0)
+    assert c.room_for_private(8) and not c.room_for_private(9)
+    p = c.take_private(6)  # evicts doc 0
+    assert len(p) == 6 and 0 not in c and c.used == 6
+    c.give_back_private(p)
+    assert c.used == 0
+
+
+def test_layout_places_documents_consecutively():
+    lay = layout_request([([1, 2], 20), ([3], 5)], [9], 3)
+    assert [(s.pos0, s.length, s.ctx) for s in lay.segments] == [(0, 20, True), (20, 5, True), (25, 3, False)]
+    assert lay.length == 28 and lay.num_tiles == 4
