@@ -200,14 +200,21 @@ class DecodeScenario(_Base):
         self._inputs[step] = t
         return t
 
-    def step(self, step: int, stream=None) -> torch.Tensor:
-        """Device work of one decode step: kv-write of the new token (q in place), then attention."""
+    def step(self, step: int, stream=None, events=None) -> torch.Tensor:
+        """Device work of one decode step: kv-write of the new token (q in place), then attention.
+
+        ``events`` = (start, end) CUDA events recorded around the attention call only."""
         q0, k, v, pos, slots = self._inputs[step] if step in self._inputs else self.stage_inputs(step)
         self.q.copy_(q0)
         self.eng.kv_write(k, v, self.q, pos, slots, stream=stream)
         tt = self.tables[step] if self.tables is not None else self.table(step)
-        return self.eng.decode(tt, self.q, pos, out=self.out, pos=self.eng.pos.with_flags(self.prerotated),
-                               stream=stream)
+        if events is not None:
+            events[0].record()
+        out = self.eng.decode(tt, self.q, pos, out=self.out, pos=self.eng.pos.with_flags(self.prerotated),
+                              stream=stream)
+        if events is not None:
+            events[1].record()
+        return out
 
     def kv_bytes(self, step: int) -> float:
         """Algorithmic HBM bytes of one decode step (K and V of every visible token, q in, out)."""
