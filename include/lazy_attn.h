@@ -182,9 +182,10 @@ lazy_status lazy_kv_write(const lazy_geom* geom, const lazy_pos_desc* pos, void*
 
 /* Bytes of device workspace lazy_attn_prefill / lazy_attn_decode need for
  * these sizes (0 if no workspace is needed).  is_prefill = 0: decode, one
- * query token per request (max_q_len ignored). */
+ * query token per request (max_q_len ignored).  max_tiles and total_tiles
+ * must be the values later passed to the attention call. */
 size_t lazy_attn_workspace_size(const lazy_geom* geom, int32_t num_reqs, int32_t max_q_len, int32_t max_tiles,
-                                int32_t is_prefill);
+                                int64_t total_tiles, int32_t is_prefill);
 
 /* Prefill over cached documents + private suffix ([N] "Key designs":
  * prefill kernel, compute-bound; [G] "Implementazione Tecnica" item 1).
@@ -199,14 +200,18 @@ size_t lazy_attn_workspace_size(const lazy_geom* geom, int32_t num_reqs, int32_t
  * n <= m.  Output out[q rows][Hq][dh] (device, T) = softmax(scale q k'^T +
  * bias) V, k' = the key at its global position (RoPE: rotation by the
  * tile's Delta inside the kernel).
- * Host sizing hints: max_q_len >= every request's query count (required),
- * max_tiles ~ the largest tile count (performance only).
+ * Host sizing hints: max_q_len >= every request's query count (required);
+ * max_tiles ~ the largest tile count and total_tiles ~ tile_start[num_reqs]
+ * (0 = unknown) size the split-K plan: each request gets one split per
+ * chunk of tiles, so long and short requests finish together.  Wrong tile
+ * hints cost speed, never correctness.
  * workspace (device) of ws_bytes >= lazy_attn_workspace_size(..., 1). */
 lazy_status lazy_attn_prefill(const lazy_geom* geom, const lazy_pos_desc* pos, const void* k_cache,
                               const void* v_cache, int64_t num_blocks, const uint64_t* tiles,
                               const int32_t* tile_start, const int32_t* ctx_tiles, const void* q,
                               const int32_t* q_start, const int32_t* q_pos0, int32_t num_reqs, int32_t max_q_len,
-                              int32_t max_tiles, void* out, void* workspace, size_t ws_bytes, void* stream);
+                              int32_t max_tiles, int64_t total_tiles, void* out, void* workspace, size_t ws_bytes,
+                              void* stream);
 
 /* Decode: one new query token per request ([N] "Key designs": decode kernel,
  * bandwidth-bound, M = 1; the query is re-rotated only when the tile's
@@ -214,13 +219,13 @@ lazy_status lazy_attn_prefill(const lazy_geom* geom, const lazy_pos_desc* pos, c
  * q: device T [num_reqs][Hq][dh], already rotated at its global position
  * q_pos[r] (device int32 [num_reqs]; read for ALiBi only).  Every valid slot
  * of every tile of the request is visible.  out: device T [num_reqs][Hq][dh].
- * Split-K over tiles with a log-sum-exp combine; max_tiles sizes the split
- * count (performance only).  workspace as for prefill (is_prefill = 0). */
+ * Split-K over tiles with a log-sum-exp combine, planned from the max_tiles /
+ * total_tiles hints as for prefill.  workspace as for prefill (is_prefill = 0). */
 lazy_status lazy_attn_decode(const lazy_geom* geom, const lazy_pos_desc* pos, const void* k_cache,
                              const void* v_cache, int64_t num_blocks, const uint64_t* tiles,
                              const int32_t* tile_start, const int32_t* ctx_tiles, const void* q,
-                             const int32_t* q_pos, int32_t num_reqs, int32_t max_tiles, void* out, void* workspace,
-                             size_t ws_bytes, void* stream);
+                             const int32_t* q_pos, int32_t num_reqs, int32_t max_tiles, int64_t total_tiles,
+                             void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /* Test hook: run the attention kernels' own device-side word unpack on n
  * device words; write device int32 block[n], offset[n], mask[n]. */

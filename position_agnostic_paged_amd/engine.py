@@ -66,6 +66,7 @@ class TileTable:
         self.host_tiles, self.host_start, self.host_ctx = tiles, tstart, nctx
         self.num_reqs = len(layouts)
         self.max_tiles = int(np.max(np.diff(tstart))) if len(layouts) else 0
+        self.total_tiles = int(tstart[-1]) if len(layouts) else 0
         self.tiles = torch.from_numpy(tiles.view(np.int64) if tiles.size else np.zeros(1, np.int64)).to(device)
         self.tile_start = torch.from_numpy(tstart).to(device)
         self.ctx_tiles = torch.from_numpy(nctx if nctx.size else np.zeros(1, np.int32)).to(device)
@@ -134,17 +135,18 @@ class Engine:
                 out: Optional[torch.Tensor] = None, pos: Optional[L.PosDescC] = None, stream=None) -> torch.Tensor:
         if out is None:
             out = torch.empty_like(q)
-        ws = self._workspace(L.workspace_size(self.geom, tt.num_reqs, max_q_len, tt.max_tiles, True))
+        ws = self._workspace(L.workspace_size(self.geom, tt.num_reqs, max_q_len, tt.max_tiles, tt.total_tiles, True))
         L.attn_prefill(self.geom, self.pos.c if pos is None else pos, self.k_cache, self.v_cache, self.num_blocks,
                        tt.tiles, tt.tile_start, tt.ctx_tiles, q, q_start, q_pos0, tt.num_reqs, max_q_len, tt.max_tiles,
-                       out, ws, stream)
+                       tt.total_tiles, out, ws, stream)
         return out
 
     def decode(self, tt: TileTable, q: torch.Tensor, q_pos: torch.Tensor, out: Optional[torch.Tensor] = None,
                pos: Optional[L.PosDescC] = None, stream=None) -> torch.Tensor:
         if out is None:
             out = torch.empty_like(q)
-        ws = self._workspace(L.workspace_size(self.geom, tt.num_reqs, 1, tt.max_tiles, False))
+        ws = self._workspace(L.workspace_size(self.geom, tt.num_reqs, 1, tt.max_tiles, tt.total_tiles, False))
         L.attn_decode(self.geom, self.pos.c if pos is None else pos, self.k_cache, self.v_cache, self.num_blocks,
-                      tt.tiles, tt.tile_start, tt.ctx_tiles, q, q_pos, tt.num_reqs, tt.max_tiles, out, ws, stream)
+                      tt.tiles, tt.tile_start, tt.ctx_tiles, q, q_pos, tt.num_reqs, tt.max_tiles, tt.total_tiles, out,
+                      ws, stream)
         return out

@@ -18,7 +18,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblazyattn.so")
+# LAZY_ATTN_LIB selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("LAZY_ATTN_LIB") or os.path.join(_HERE, "liblazyattn.so")
 
 LAZY_OK, LAZY_ERR_ARG, LAZY_ERR_UNSUPPORTED, LAZY_ERR_WORKSPACE, LAZY_ERR_HIP = 0, -1, -2, -3, -4
 LAZY_BF16, LAZY_FP32 = 0, 1
@@ -69,15 +70,15 @@ def lib() -> C.CDLL:
             "lazy_unpack_tiles": [P, I64, P, P, P],
             "lazy_build_tiles": [I32, I32, P, P, P, P, P, P, I64, P, I64, P, P],
             "lazy_kv_write": [P, P, P, P, I64, P, P, P, P, P, I32, P],
-            "lazy_attn_prefill": [P, P, P, P, I64, P, P, P, P, P, P, I32, I32, I32, P, P, C.c_size_t, P],
-            "lazy_attn_decode": [P, P, P, P, I64, P, P, P, P, P, I32, I32, P, P, C.c_size_t, P],
+            "lazy_attn_prefill": [P, P, P, P, I64, P, P, P, P, P, P, I32, I32, I32, I64, P, P, C.c_size_t, P],
+            "lazy_attn_decode": [P, P, P, P, I64, P, P, P, P, P, I32, I32, I64, P, P, C.c_size_t, P],
             "lazy_debug_unpack": [P, I64, P, P, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = I32
-        L.lazy_attn_workspace_size.argtypes = [P, I32, I32, I32, I32]
+        L.lazy_attn_workspace_size.argtypes = [P, I32, I32, I32, I64, I32]
         L.lazy_attn_workspace_size.restype = C.c_size_t
         L.lazy_last_error.argtypes = []
         L.lazy_last_error.restype = C.c_char_p
@@ -185,25 +186,28 @@ def kv_write(geom: Geom, pos: PosDescC, k_cache, v_cache, num_blocks: int, k, v,
                                _dev(v), _dev(q_inout), _dev(positions), _dev(slot_mapping), n, _stream(stream)))
 
 
-def workspace_size(geom: Geom, num_reqs: int, max_q_len: int, max_tiles: int, is_prefill: bool) -> int:
-    return int(lib().lazy_attn_workspace_size(C.byref(geom), num_reqs, max_q_len, max_tiles, int(is_prefill)))
+def workspace_size(geom: Geom, num_reqs: int, max_q_len: int, max_tiles: int, total_tiles: int,
+                   is_prefill: bool) -> int:
+    return int(lib().lazy_attn_workspace_size(C.byref(geom), num_reqs, max_q_len, max_tiles, total_tiles,
+                                              int(is_prefill)))
 
 
 def attn_prefill(geom: Geom, pos: PosDescC, k_cache, v_cache, num_blocks: int, tiles, tile_start, ctx_tiles, q,
-                 q_start, q_pos0, num_reqs: int, max_q_len: int, max_tiles: int, out, workspace, stream=None):
+                 q_start, q_pos0, num_reqs: int, max_q_len: int, max_tiles: int, total_tiles: int, out, workspace,
+                 stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().lazy_attn_prefill(C.byref(geom), C.byref(pos), _dev(k_cache), _dev(v_cache), num_blocks,
                                    _dev(tiles), _dev(tile_start), _dev(ctx_tiles), _dev(q), _dev(q_start),
-                                   _dev(q_pos0), num_reqs, max_q_len, max_tiles, _dev(out), _dev(workspace), ws_bytes,
-                                   _stream(stream)))
+                                   _dev(q_pos0), num_reqs, max_q_len, max_tiles, total_tiles, _dev(out),
+                                   _dev(workspace), ws_bytes, _stream(stream)))
 
 
 def attn_decode(geom: Geom, pos: PosDescC, k_cache, v_cache, num_blocks: int, tiles, tile_start, ctx_tiles, q, q_pos,
-                num_reqs: int, max_tiles: int, out, workspace, stream=None):
+                num_reqs: int, max_tiles: int, total_tiles: int, out, workspace, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().lazy_attn_decode(C.byref(geom), C.byref(pos), _dev(k_cache), _dev(v_cache), num_blocks, _dev(tiles),
                                   _dev(tile_start), _dev(ctx_tiles), _dev(q), _dev(q_pos), num_reqs, max_tiles,
-                                  _dev(out), _dev(workspace), ws_bytes, _stream(stream)))
+                                  total_tiles, _dev(out), _dev(workspace), ws_bytes, _stream(stream)))
 
 
 def debug_unpack(words, block, offset, mask, stream=None):

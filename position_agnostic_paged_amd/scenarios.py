@@ -78,10 +78,19 @@ class _Base:
         self.tdtype = TORCH_DTYPE[wl.geom.dtype]
         self.dev = engine.device
         self.doc_writes = 0
+        self._staged = {}  # raw document contents on the device (private copies reuse them)
 
     def _doc_dev(self, d: int):
+        if d in self._staged:
+            return self._staged[d]
         k, v = self.wl.doc(d, cache=False)
-        return _to_dev(k, self.tdtype, self.dev), _to_dev(v, self.tdtype, self.dev)
+        kv = (_to_dev(k, self.tdtype, self.dev), _to_dev(v, self.tdtype, self.dev))
+        if not self.shared:
+            self._staged[d] = kv
+        return kv
+
+    def release_staging(self) -> None:
+        self._staged.clear()
 
     def _doc_segments(self, doc_ids: Sequence[int]) -> List[Segment]:
         """Context segments of a request, placed consecutively from position 0."""

@@ -168,7 +168,7 @@ def test_device_calls_validate_before_launch(L):
 
     def prefill(geom, pos, nb=10, nreq=1, maxq=4):
         return lib.lazy_attn_prefill(C.byref(geom), C.byref(pos), fake, fake, nb, fake, fake, fake, fake, fake, fake,
-                                     nreq, maxq, 512, fake, None, 0, None)
+                                     nreq, maxq, 512, 0, fake, None, 0, None)
 
     assert prefill(L.make_geom(30, 8, 128, "bf16"), p) == L.LAZY_ERR_ARG  # Hq % Hkv
     assert prefill(L.make_geom(32, 8, 96, "bf16"), p) == L.LAZY_ERR_UNSUPPORTED  # head_dim
@@ -182,11 +182,11 @@ def test_device_calls_validate_before_launch(L):
     assert prefill(g, L.PosDescC(0, 0, 10, 0.1, None, None, None)) == L.LAZY_ERR_ARG  # RoPE without coefficients
     assert prefill(g, L.PosDescC(0, 4, 10, 0.1, 1, None, None)) == L.LAZY_ERR_ARG  # unknown flag
     # a split plan needs a workspace: none given
-    assert L.workspace_size(g, 1, 4, 512, True) > 0
+    assert L.workspace_size(g, 1, 4, 512, 0, True) > 0
     assert prefill(g, p) == L.LAZY_ERR_WORKSPACE
     assert "workspace" in L.last_error()
     # decode with too small a workspace
-    assert lib.lazy_attn_decode(C.byref(g), C.byref(p), fake, fake, 10, fake, fake, fake, fake, fake, 64, 2048,
+    assert lib.lazy_attn_decode(C.byref(g), C.byref(p), fake, fake, 10, fake, fake, fake, fake, fake, 64, 2048, 0,
                                 fake, fake, 16, None) == L.LAZY_ERR_WORKSPACE
     # kv write: negative count, empty is a no-op
     assert lib.lazy_kv_write(C.byref(g), C.byref(p), fake, fake, 10, fake, fake, None, fake, fake, -1,

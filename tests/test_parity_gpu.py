@@ -108,3 +108,108 @@ def test_falcon_alibi_decode_sampled():
     rng = np.random.default_rng(5)
     reqs = sorted(rng.choice(128, size=12, replace=False).tolist())
     _check_decode("falcon7b_alibi", steps=[0, 7], reqs=reqs, num_steps=8)
+
+
+def test_ragged_prefill():
+    """Questions of 1..64 tokens (two row tiles), a request with no document, 1..999-token documents."""
+    _check_prefill("ragged")
+
+
+def test_ragged_decode_uneven_splits():
+    """Requests from 7 to 11K tokens: per-request split counts differ inside one launch."""
+    _check_decode("ragged", steps=[0, 2, 4])
+
+
+def test_llama8b_prefill_on_the_fly_sincos():
+    _check_prefill("llama8b_prefill", on_the_fly=True)
+
+
+def test_mixed_yarn_prefill_step0():
+    """YaRN x8 (original 8192) 70B shape: 4 prefills of 15 x 500-token documents + 64-token questions."""
+    from workloads import gen
+
+    wl = gen._mixed_llama70b(num_steps=1)
+    wl.decode_reqs = []
+    _check_prefill_wl(wl)
+
+
+def test_mixed_yarn_decode_sampled():
+    """48 decodes at 8K-66K context (YaRN), sampled requests including the longest."""
+    from workloads import gen
+
+    wl = gen._mixed_llama70b(num_steps=3)
+    wl.prefill_steps = []
+    lens = [wl.decode_ctx_len(r) for r in range(len(wl.decode_reqs))]
+    reqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 7, 30})
+    _check_decode_wl(wl, steps=[0, 2], reqs=reqs)
+
+
+def _check_prefill_wl(wl):
+    from position_agnostic_paged_amd.scenarios import PrefillScenario
+
+    say(f"[prefill parity] {wl.name}")
+    eng = _engine(wl)
+    sc = PrefillScenario(wl, eng)
+    out = sc.run().float().cpu().numpy()
+    want = oracle_prefill(wl, 0, range(len(sc.reqs)))
+    err = max(max_abs(out[sc.q_start_h[i]: sc.q_start_h[i + 1]], w) for i, w in enumerate(want))
+    say(f"  max-abs err {err:.3e} (tol {TOL[wl.geom.dtype]})")
+    assert err <= TOL[wl.geom.dtype]
+
+
+def _check_decode_wl(wl, steps, reqs):
+    from position_agnostic_paged_amd.scenarios import DecodeScenario
+
+    say(f"[decode parity] {wl.name} steps={steps} reqs={reqs}")
+    eng = _engine(wl)
+    sc = DecodeScenario(wl, eng)
+    draws, got = {}, {}
+    for s in range(max(steps) + 1):
+        draws[s] = wl.decode_step(s)
+        out = sc.step(s)
+        if s in steps:
+            got[s] = out.float().cpu().numpy()
+    err = 0.0
+    for r in reqs:
+        for s, w in zip(steps, oracle_decode(wl, r, steps, draws)):
+            err = max(err, max_abs(got[s][r], w))
+    say(f"  max-abs err {err:.3e} (tol {TOL[wl.geom.dtype]})")
+    assert err <= TOL[wl.geom.dtype]
+
+
+def test_device_unpack_bit_exact():
+    """The kernels' own word split (through lazy_debug_unpack) equals the oracle's on boundary + random words."""
+    from oracle import pack as OP
+    from position_agnostic_paged_amd import lazy_attn as L
+
+    rng = np.random.default_rng(21)
+    vals = [(0, 0, 1), ((1 << 24) - 1, (1 << 24) - 1, 0xFFFF), (0, 0, 0x8000), (123, 456, 0x0F0F)]
+    vals += [(int(b), int(o), int(m)) for b, o, m in zip(rng.integers(0, 1 << 24, 100000),
+                                                          rng.integers(0, 1 << 24, 100000),
+                                                          rng.integers(1, 1 << 16, 100000))]
+    words = np.array([OP.pack(*v) for v in vals], dtype=np.uint64)
+    wd = torch.from_numpy(words.view(np.int64)).cuda()
+    n = len(vals)
+    blk, off, msk = (torch.empty(n, dtype=torch.int32, device="cuda") for _ in range(3))
+    L.debug_unpack(wd, blk, off, msk)
+    got = np.stack([blk.cpu().numpy(), off.cpu().numpy(), msk.cpu().numpy()], 1).astype(np.int64)
+    assert np.array_equal(got, np.array(vals, dtype=np.int64))
+
+
+def test_attention_never_writes_the_cache():
+    """Zero-copy reuse: prefill and decode read cached documents in place and leave the pools byte-identical."""
+    from position_agnostic_paged_amd.scenarios import DecodeScenario, PrefillScenario
+
+    wl = make_workload("ragged")
+    eng = _engine(wl)
+    sc = PrefillScenario(wl, eng)
+    dec = DecodeScenario(wl, eng, num_steps=2)
+    dec.step(0)  # writes its token
+    torch.cuda.synchronize()
+    kb, vb = eng.k_cache.clone(), eng.v_cache.clone()
+    for _ in range(3):
+        sc.run()
+        eng.decode(dec.table(0), dec.q, torch.from_numpy(dec.positions(0)).cuda(), out=dec.out)
+    torch.cuda.synchronize()
+    assert torch.equal(kb.view(torch.int16), eng.k_cache.view(torch.int16))
+    assert torch.equal(vb.view(torch.int16), eng.v_cache.view(torch.int16))

@@ -267,7 +267,35 @@ def _falcon_alibi() -> Workload:
     return wl
 
 
+def _ragged() -> Workload:
+    """Edge cases: uneven requests, partial blocks, questions of 1..64 tokens, a request with no document."""
+    wl = Workload(
+        name="ragged_bf16_h8kv2_d128",
+        wid=7,
+        geom=Geometry(8, 2, 128, "bf16"),
+        pos=PosSpec("rope_half", base=5e5),
+        kv_scale=0.5,
+        doc_lens={d: [300, 17, 1, 250, 16, 999][d % 6] for d in range(60)},
+        num_decode_steps=5,
+        description="ragged lengths: documents of 1..999 tokens, 0..40 per request, questions of 1..64 tokens",
+    )
+    pre = []
+    for r, (ndoc, lq) in enumerate([(0, 5), (3, 1), (5, 64), (1, 33), (6, 17)]):
+        pr = _question(wl, [r], lq, True)
+        pr.doc_ids = _zipf_pick(7, [r], 60, ndoc, 1.0) if ndoc else []
+        pre.append(pr)
+    wl.prefill_steps = [pre]
+    decs = []
+    for r, (ndoc, lq) in enumerate([(1, 0), (40, 3), (2, 16), (12, 0), (0, 7), (25, 1)]):
+        dr = _question(wl, [100 + r], lq, False)
+        dr.doc_ids = _zipf_pick(7, [100 + r], 60, ndoc, 1.0) if ndoc else []
+        decs.append(dr)
+    wl.decode_reqs = decs
+    return wl
+
+
 WORKLOADS = {
+    "ragged": _ragged,
     "tiny_fp32": _tiny_fp32,
     "llama8b_prefill": lambda: _prefill_llama8b("rope_half", 2, "llama8b_prefill_b8_10x200"),
     "llama8b_decode": _decode_llama8b,
