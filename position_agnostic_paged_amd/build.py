@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblazyattn.so")
 
-SOURCES = ["attention.hip", "kv_write.hip", "host.cpp"]
+SOURCES = ["attention.hip", "prefill_lds.hip", "kv_write.hip", "host.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU forms are disabled for all device code.
