@@ -25,13 +25,17 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU forms are disabled for all device code.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-result"]
+# Per-source extras.  The staged prefill never tests for NaN, so it runs with
+# the IEEE mode bit off: min/max then take operands as they are instead of
+# quieting each one first (infinities keep their meaning).
+EXTRA = {"prefill_lds.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-c", *COMMON, *DEVICE_FLAGS, path, "-o", obj]
+        cmd = [HIPCC, "-c", *COMMON, *DEVICE_FLAGS, *EXTRA.get(src, []), path, "-o", obj]
     else:
         cmd = [HIPCC, "-c", *COMMON, "-x", "c++", path, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,23 +1,26 @@
 // LDS-staged prefill over a position-agnostic paged cache (bf16, gfx950).
 //
-// Same computation as the per-wave prefill (LazyAttention notes,
-// papernotes.org, "Key designs": compute-bound prefill with the document
-// offset applied inside the fused kernel), organised for CDNA4:
+// Same computation as the per-wave prefill, organised as the pages' prefill
+// kernel (LazyAttention notes, papernotes.org, "Key designs": the K tile is
+// staged in shared memory and rotated there by the document offset Delta
+// before the matrix products), adapted to CDNA4:
 //
 //   * a workgroup = NW waves x RB blocks of 16 GQA-packed query rows of one
 //     (request, KV head); all waves consume the same tile pairs;
 //   * each tile pair (K 2 x 16 x dh, V 2 x dh x 16, plus the two cos/sin
 //     rows of the pair's document offsets) is copied once per workgroup
 //     from HBM into LDS with direct global->LDS loads (no registers), into a
-//     ring of kStages buffers, so kStages-1 pairs are in flight while one is
-//     consumed by the MFMAs;
+//     ring of kStages buffers that fills the 160 KiB LDS, so kStages-3 pairs
+//     are in flight while one pair is rotated, the next one's scores are
+//     computed and the one before it is consumed (the copies are
+//     latency-bound: bytes in flight set the rate);
+//   * once a pair has landed, the workgroup rotates its context K rows in
+//     place by R_Delta (fp32 arithmetic, rounded back to bf16), turning the
+//     position-agnostic R_j k into R_(Delta+j) k; the query stays at its
+//     global position in registers for the whole loop;
 //   * LDS rows are XOR-swizzled at 16-byte granularity so the per-lane
-//     fragment reads (16 B of a K row, 8 B of a V channel row) are free of
+//     fragment reads (16 B of a K row, 16 B of a V channel row) are free of
 //     bank conflicts;
-//   * the query is re-rotated by -Delta once per document from the raw
-//     query parked in LDS and the cos/sin row in the stage, so the loop
-//     issues no global load besides the stage copies (keeping the counted
-//     waits on the copies exact);
 //   * the softmax is trimmed for the matrix cores: pairs of two full
 //     document tiles (the bulk of a long context) skip masking; the row max
 //     is taken on raw scores against a per-row threshold, so the cross-lane
@@ -27,19 +30,30 @@
 //     sum of exactly the bf16 weights that multiply V).
 #include "attn_common.hpp"
 
-#ifndef LAZY_PREFILL_LDS_WAVES
-#define LAZY_PREFILL_LDS_WAVES 8  // waves per workgroup (8: two per SIMD, 4: one)
-#endif
-
 namespace lazy {
 
-constexpr int kStages = 4;  // LDS ring of tile pairs
+constexpr int kPrefillWaves = 8;         // waves per workgroup: two per SIMD
+constexpr int kLdsBytes = 160 * 1024;    // LDS of one CU, all of it for the ring
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most n stages of L copies each are outstanding (n <= MAXN).
+template <int L, int MAXN>
+__device__ __forceinline__ void wait_stages(int n) {
+  if constexpr (MAXN > 0) {
+    if (n >= MAXN) {
+      wait_vmcnt<MAXN * L>();
+      return;
+    }
+    wait_stages<L, MAXN - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
 }
 
 template <int DH, bool ROT, int NW>
@@ -53,12 +67,57 @@ struct StageGeom {
   static constexpr int kKChunks = 2 * kTile / 16;    // 16-B chunks of the K pair (same for V)
   static constexpr int kCopies = 2 * kKChunks / (NW * 64);  // K + V copies per thread
   static constexpr int kLoads = kCopies + (ROT ? 1 : 0);    // copies per wave per stage
+  static constexpr int kStages = (kLdsBytes / kBytes) < 10 ? (kLdsBytes / kBytes) : 10;
   // every wave issues the same number of copies (the counted waits rely on
   // it) and no wave's 64 chunks straddle the K / V boundary
   static_assert(kCopies >= 1 && (2 * kKChunks) % (NW * 64) == 0 && kKChunks % 64 == 0, "stage copy shape");
+  static_assert(kStages >= 5 && (kStages - 3) * kLoads < 64, "ring depth");
+  // rotation items: 16 rows x dh/8 items (4 rotation pairs each) per tile
+  static constexpr int kRotItems = kBlock * DH / 8;
+  static_assert(kRotItems % 64 == 0, "rotation items per wave");
 };
 
 typedef const __attribute__((address_space(4))) uint64_t* const_words;
+
+// Raw tile words of one pair (the second is 0 -- an empty tile -- past the
+// split's end).
+struct PairWords {
+  uint64_t w0, w1;
+};
+
+// K row swizzle: the 16-byte chunk q of row t of tile x sits at chunk
+// position q ^ key; tile 1 uses keys disjoint from tile 0's for the rows one
+// fragment read touches together.
+template <int DH>
+__device__ __forceinline__ int k_key(int t, int x) {
+  return (t ^ (4 * x)) % (DH / 8);
+}
+
+// Workgroup -> work unit.  The workgroups of one (request, KV head, split)
+// -- its row tiles -- read the same K/V tiles, so they are placed on one XCD
+// (dispatch deals workgroups round-robin over the 8 XCDs, each with its own
+// L2) and dispatched close together: the second reader finds the tiles in
+// L2.  A 1-D grid of units x row_tiles workgroups; with a unit count that is
+// not a multiple of 8 the plain order is used.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ void xcd_unit(int wg, int num_wgs, int splits, int hkv, int row_tiles, int& req, int& kvh,
+                                         int& split, int& row_tile) {
+  const int units = num_wgs / row_tiles;
+  int u, t;
+  if (units % kXcds == 0) {
+    const int k = wg / kXcds;
+    t = k % row_tiles;
+    u = (k / row_tiles) * kXcds + wg % kXcds;
+  } else {
+    u = wg / row_tiles;
+    t = wg % row_tiles;
+  }
+  split = u % splits;
+  kvh = (u / splits) % hkv;
+  req = u / (splits * hkv);
+  row_tile = t;
+}
 
 template <int DH, int KIND, bool DEFER, int RB, int NW>
 struct LdsPrefill {
@@ -68,21 +127,55 @@ struct LdsPrefill {
   static constexpr int NV = DH / 16;  // 16-channel blocks of the output
   static constexpr bool kRot = (KIND != kAlibi) && DEFER;
   using SG = StageGeom<DH, kRot, NW>;
+  static constexpr int S = SG::kStages;
 
   const AttnArgs& a;
   unsigned char* lds;
-  int tid, lane, wave, r, g, kvh, sb, se, nctx;
+  int tid, lane, wave, kvh, sb, se, nctx, npairs;
   // The tile table is read-only for the kernel's lifetime, so it is read
   // through the constant address space: scalar loads, counted apart from the
   // stage copies.
   const_words words;
+  uint32_t copy_off[SG::kCopies];  // per-lane byte offset of each stage copy in its tile
 
-  // tile words of pair p, decoded with the device-side guards
-  __device__ __forceinline__ void pair_meta(int p, TileMeta (&mt)[2], int (&delta)[2], bool (&priv)[2]) const {
-    const int ia = sb + 2 * p;
-    mt[0] = unpack_word(words[ia]);
-    mt[1] = unpack_word(words[min(ia + 1, se - 1)]);
-    if (ia + 1 >= se) mt[1].mask = 0u;
+  __device__ __forceinline__ void init_copies() {
+#pragma unroll
+    for (int i = 0; i < SG::kCopies; ++i) {
+      const int cb = (i * NW + wave) * 64;  // wave-uniform first chunk
+      const bool is_v = cb >= SG::kKChunks;
+      const int cv = (is_v ? cb - SG::kKChunks : cb) + lane;
+      const int x = cv / (SG::kTile / 16);
+      const int cc = cv % (SG::kTile / 16);
+      int elem;
+      if (!is_v) {
+        const int row = cc / SG::kChunksPerRow, pos = cc % SG::kChunksPerRow;
+        elem = row * DH + (pos ^ k_key<DH>(row, x)) * 8;
+      } else {  // V rows are channels of 16 tokens = 2 chunks
+        const int row = cc >> 1, pos = cc & 1;
+        elem = row * kBlock + (pos ^ ((row >> 3) & 1)) * 8;
+      }
+      copy_off[i] = (uint32_t)elem * 2u;
+    }
+  }
+
+  __device__ __forceinline__ unsigned char* stage(int q) const { return lds + (q % S) * SG::kBytes; }
+
+  __device__ __forceinline__ PairWords load_words(int q) const {
+    PairWords pw{0ull, 0ull};
+    if (q < npairs) {
+      const int ia = sb + 2 * q;
+      pw.w0 = words[ia];
+      if (ia + 1 < se) pw.w1 = words[ia + 1];
+    }
+    return pw;
+  }
+
+  // tile words of a pair, decoded with the device-side guards
+  __device__ __forceinline__ void pair_meta(int q, const PairWords& pw, TileMeta (&mt)[2], int (&delta)[2],
+                                            bool (&priv)[2]) const {
+    const int ia = sb + 2 * q;
+    mt[0] = unpack_word(pw.w0);
+    mt[1] = unpack_word(pw.w1);
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       priv[x] = ia + x >= nctx;
@@ -98,35 +191,24 @@ struct LdsPrefill {
     }
   }
 
-  // copy pair p into stage buffer p % kStages (every wave issues SG::kLoads copies)
-  __device__ __forceinline__ void issue(int p) const {
+  // copy pair q into its stage buffer (every wave issues SG::kLoads copies)
+  __device__ __forceinline__ void issue(int q, const PairWords& pw) const {
     TileMeta mt[2];
     int delta[2];
     bool priv[2];
-    pair_meta(p, mt, delta, priv);
-    unsigned char* st = lds + (p % kStages) * SG::kBytes;
-    const bf16* kc = reinterpret_cast<const bf16*>(a.k_cache);
-    const bf16* vc = reinterpret_cast<const bf16*>(a.v_cache);
+    pair_meta(q, pw, mt, delta, priv);
+    unsigned char* st = stage(q);
 #pragma unroll
     for (int i = 0; i < SG::kCopies; ++i) {
       // chunk ci of the stage's K pair, then V pair; the LDS slot of a copy
       // is the wave's base plus 16 B per lane, i.e. stage offset 16 * ci
-      const int ci = i * NW * 64 + tid;
-      const bool is_v = ci >= SG::kKChunks;  // wave-uniform
-      const int cv = is_v ? ci - SG::kKChunks : ci;
-      const int x = cv / (SG::kTile / 16);
-      const int cc = cv % (SG::kTile / 16);
+      const int cb = (i * NW + wave) * 64;
+      const bool is_v = cb >= SG::kKChunks;
+      const int x = (is_v ? cb - SG::kKChunks : cb) / (SG::kTile / 16);
       const int blk = x ? mt[1].block : mt[0].block;
-      const int64_t base = ((int64_t)blk * a.hkv + kvh) * (kBlock * DH);
-      const bf16* src;
-      if (!is_v) {
-        const int row = cc / SG::kChunksPerRow, pos = cc % SG::kChunksPerRow;
-        src = kc + base + row * DH + (pos ^ (row % SG::kChunksPerRow)) * 8;
-      } else {  // V rows are channels of 16 tokens = 2 chunks
-        const int row = cc >> 1, pos = cc & 1;
-        src = vc + base + row * kBlock + (pos ^ ((row >> 3) & 1)) * 8;
-      }
-      __builtin_amdgcn_global_load_lds(src, st + (i * NW + wave) * 64 * 16, 16, 0, 0);
+      const char* base = reinterpret_cast<const char*>(is_v ? a.v_cache : a.k_cache) +
+                         ((int64_t)blk * a.hkv + kvh) * (int64_t)(kBlock * DH * 2);
+      __builtin_amdgcn_global_load_lds(base + copy_off[i], st + cb * 16, 16, 0, 0);
     }
     if (kRot) {
       // the two cos/sin rows: DH/4 chunks each; wave w copies its share (lane-masked)
@@ -143,79 +225,101 @@ struct LdsPrefill {
     }
   }
 
-  // the wave's parked raw query fragment (b, c)
-  __device__ __forceinline__ F8 raw_at(const unsigned char* raw, int b, int c) const {
-    return *reinterpret_cast<const F8*>(raw + ((b * NC + c) * 64 + lane) * 16);
+  // R_Delta applied in place to the context K rows of a landed pair: each
+  // thread takes 4 rotation pairs of one row (half-split: dims 4u..4u+3 with
+  // their partners dh/2 away; interleaved: dims 8u..8u+7).  Tiles with
+  // Delta = 0 (private tokens, a document at position 0, dropped tiles) are
+  // already at their global positions.
+  __device__ __forceinline__ void rotate_stage(int q, const PairWords& pw) const {
+    if (!kRot) return;
+    TileMeta mt[2];
+    int delta[2];
+    bool priv[2];
+    pair_meta(q, pw, mt, delta, priv);
+    unsigned char* st = stage(q);
+#pragma unroll
+    for (int it0 = 0; it0 < 2 * SG::kRotItems; it0 += NW * 64) {
+      const int wbase = it0 + wave * 64;  // wave-uniform
+      if (wbase >= 2 * SG::kRotItems) break;
+      const int x = wbase / SG::kRotItems;
+      if ((x ? delta[1] : delta[0]) == 0) continue;
+      const int i = wbase % SG::kRotItems + lane;
+      const int t = i / (DH / 8), u = i % (DH / 8);
+      const float* cs = reinterpret_cast<const float*>(st + SG::kCS) + x * DH;
+      unsigned char* row = st + SG::kK + x * SG::kTile + t * (DH * 2);
+      const int key = k_key<DH>(t, x);
+      if (KIND == kHalf) {
+        const f32x4 c = *reinterpret_cast<const f32x4*>(cs + 4 * u);
+        const f32x4 s = *reinterpret_cast<const f32x4*>(cs + DH / 2 + 4 * u);
+        F4* plo = reinterpret_cast<F4*>(row + ((((4 * u) / 8) ^ key) << 4) + ((u & 1) << 3));
+        F4* phi = reinterpret_cast<F4*>(row + ((((4 * u + DH / 2) / 8) ^ key) << 4) + ((u & 1) << 3));
+        const F4 lo = *plo, hi = *phi;
+        F4 nlo, nhi;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x1 = (float)lo[k], x2 = (float)hi[k];
+          nlo[k] = (bf16)(x1 * c[k] - x2 * s[k]);
+          nhi[k] = (bf16)(x2 * c[k] + x1 * s[k]);
+        }
+        *plo = nlo;
+        *phi = nhi;
+      } else {
+        const f32x4 c = *reinterpret_cast<const f32x4*>(cs + 4 * u);
+        const f32x4 s = *reinterpret_cast<const f32x4*>(cs + DH / 2 + 4 * u);
+        F8* pv = reinterpret_cast<F8*>(row + ((u ^ key) << 4));
+        const F8 v = *pv;
+        F8 nv;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x1 = (float)v[2 * k], x2 = (float)v[2 * k + 1];
+          nv[2 * k] = (bf16)(x1 * c[k] - x2 * s[k]);
+          nv[2 * k + 1] = (bf16)(x2 * c[k] + x1 * s[k]);
+        }
+        *pv = nv;
+      }
+    }
   }
 
-  // q' = R_{-delta} q from the parked raw query and the stage's cos/sin row x
-  __device__ __forceinline__ void rotate(F8 (&qr)[RB][NC], const unsigned char* raw, const unsigned char* st, int x,
-                                         int delta) const {
-    if (delta == 0) {
+  // Raw scores of a pair's two tiles (K rows at their global positions):
+  // s[h][b][j] = score of query row r of block b against the key whose
+  // product row the lane's koff[h] selects.
+  __device__ __forceinline__ void scores(const unsigned char* st, const uint32_t (&koff)[2][NC],
+                                         const F8 (&qr)[RB][NC], f32x4 (&s)[2][RB]) const {
 #pragma unroll
-      for (int b = 0; b < RB; ++b)
+    for (int h = 0; h < 2; ++h) {
+      F8 kf[NC];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) qr[b][c] = raw_at(raw, b, c);
-      return;
-    }
-    const float* row = reinterpret_cast<const float*>(st + SG::kCS) + x * DH;
-    if (KIND == kHalf) {
+      for (int c = 0; c < NC; ++c) kf[c] = *reinterpret_cast<const F8*>(st + koff[h][c]);
 #pragma unroll
-      for (int c = 0; c < NC / 2; ++c) {
-        const float* cp = row + 32 * c + 8 * g;
-        const f32x4 c0 = *reinterpret_cast<const f32x4*>(cp), c1 = *reinterpret_cast<const f32x4*>(cp + 4);
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(cp + DH / 2);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(cp + DH / 2 + 4);
+      for (int b = 0; b < RB; ++b) {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          const F8 lo = raw_at(raw, b, c), hi = raw_at(raw, b, c + NC / 2);
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const float cs = t < 4 ? c0[t] : c1[t - 4], sn = t < 4 ? s0[t] : s1[t - 4];
-            const float x1 = (float)lo[t], x2 = (float)hi[t];
-            qr[b][c][t] = (bf16)(x1 * cs + x2 * sn);
-            qr[b][c + NC / 2][t] = (bf16)(x2 * cs - x1 * sn);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const float* cp = row + 16 * c + 4 * g;
-        const f32x4 c0 = *reinterpret_cast<const f32x4*>(cp), s0 = *reinterpret_cast<const f32x4*>(cp + DH / 2);
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          const F8 xr = raw_at(raw, b, c);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float x1 = (float)xr[2 * u], x2 = (float)xr[2 * u + 1];
-            qr[b][c][2 * u] = (bf16)(x1 * c0[u] + x2 * s0[u]);
-            qr[b][c][2 * u + 1] = (bf16)(x2 * c0[u] - x1 * s0[u]);
-          }
-        }
+        for (int c = 0; c < NC; ++c) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qr[b][c], z, 0, 0, 0);
+        s[h][b] = z;
       }
     }
   }
 };
 
 template <int DH, int KIND, bool DEFER, int RB, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int row_tiles, int num_wgs) {
   using P = LdsPrefill<DH, KIND, DEFER, RB, NW>;
   using F8 = typename P::F8;
   using F4 = typename P::F4;
   constexpr int NC = P::NC;
   constexpr int NV = P::NV;
   using SG = typename P::SG;
+  constexpr int S = P::S;
   extern __shared__ __align__(16) unsigned char lds_buf[];
 
-  const int tid = threadIdx.x;
+  // ids through the intrinsics (no library call: a call's results would
+  // not be known to be wave-uniform)
+  const int tid = __builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int req = blockIdx.z;
-  const int kvh = blockIdx.y;
-  const int row_tile = blockIdx.x / a.num_splits;
-  const int split = blockIdx.x % a.num_splits;
+  int req, kvh, split, row_tile;
+  xcd_unit(__builtin_amdgcn_workgroup_id_x(), num_wgs, a.num_splits, a.hkv, row_tiles, req, kvh, split, row_tile);
 
   const int q0 = a.q_start[req];
   int nq = a.q_start[req + 1] - q0;
@@ -230,18 +334,18 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a) {
   if (!split_range(nt, a.chunk, a.num_splits, split, sb, se)) return;
   const int npairs = (se - sb + 1) >> 1;
   const int rb0 = (row_tile * NW + wave) * RB;
-  const bool has_rows = rb0 * 16 < nrows;  // wave-uniform: waves without rows still copy tiles
+  const bool has_rows = rb0 * 16 < nrows;  // wave-uniform: waves without rows still copy and rotate
   const int qpos0 = a.q_pos[req];
 
-  P pl{a, lds_buf, tid, lane, wave, r, g, kvh, sb, se, a.ctx_tiles[req], (const_words)(a.tiles + t0)};
+  P pl{a, lds_buf, tid, lane, wave, kvh, sb, se, a.ctx_tiles[req], npairs, (const_words)(a.tiles + t0), {}};
+  pl.init_copies();
 
-  // Query rows: row rho of the request is (token rho / G, head kvh*G + rho % G);
-  // rows past the request's last are zero (computed, never stored).  The raw
-  // query at its global position, the source of every re-rotation, is parked
-  // in this wave's LDS area (fragment order, 16 B per lane).
-  unsigned char* raw = lds_buf + kStages * SG::kBytes + wave * (RB * NC * 64 * 16);
+  // Query rows at their global positions: row rho of the request is
+  // (token rho / G, head kvh*G + rho % G); rows past the request's last are
+  // zero (computed, never stored).
   int qp[RB];
   float slope_raw[RB];
+  F8 qr[RB][NC];
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     const int rho = (rb0 + b) * 16 + r;
@@ -254,17 +358,26 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a) {
     const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + ((int64_t)(q0 + qi) * a.hq + head) * DH;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      F8 v = *reinterpret_cast<const F8*>(qrow + 32 * c + 8 * g);
-      if (!ok) v = F8{};
-      *reinterpret_cast<F8*>(raw + ((b * NC + c) * 64 + lane) * 16) = v;
+      const F8 v = *reinterpret_cast<const F8*>(qrow + 32 * c + 8 * g);
+      qr[b][c] = ok ? v : F8{};
     }
   }
-  F8 qr[RB][NC];
+
+  // Fragment offsets inside a stage (loop-invariant).  K product h, chunk c:
+  // row r of the product is key (tile r/8, token 8 ((r/4)%2) + 4h + r%4), so
+  // each lane's eight scores s[h][b][j] are the consecutive tokens
+  // 8 (g%2) + 4h + j of tile g/2 -- the slots of the lane's single 16-byte V
+  // read (channel row 16n + r of tile g/2).
+  uint32_t koff[2][NC];
 #pragma unroll
-  for (int b = 0; b < RB; ++b)
+  for (int h = 0; h < 2; ++h) {
+    const int x = r >> 3;
+    const int t = 8 * ((r >> 2) & 1) + 4 * h + (r & 3);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qr[b][c] = pl.raw_at(raw, b, c);
-  int cur_delta = 0;
+    for (int c = 0; c < NC; ++c)
+      koff[h][c] = SG::kK + x * SG::kTile + t * (DH * 2) + (((4 * c + g) ^ k_key<DH>(t, x)) << 4);
+  }
+  const uint32_t voff = SG::kV + (g >> 1) * SG::kTile + r * 32 + (((g & 1) ^ ((r >> 3) & 1)) << 4);
 
   f32x4 acc[RB][NV];
   f32x4 lsum[RB];  // row sums, replicated in the four registers
@@ -283,135 +396,131 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) ones[t] = (bf16)1.f;
 
-  // prologue: kStages - 1 pairs in flight
+  // prologue: S - 1 pairs in flight; pairs 0 and 1 landed and rotated;
+  // scores of pair 0
 #pragma unroll
-  for (int p = 0; p < kStages - 1; ++p)
-    if (p < npairs) pl.issue(p);
+  for (int q = 0; q < S - 1; ++q)
+    if (q < npairs) pl.issue(q, pl.load_words(q));
+  wait_stages<SG::kLoads, S - 3>(min(S - 3, npairs - 2));
+  asm volatile("s_barrier" ::: "memory");
+  // Tile words travel through scalar registers: pair p (consumed), p + 2
+  // (rotated) and p + S - 1 (copied) at iteration p, each read one
+  // iteration ahead.
+  PairWords wc = pl.load_words(0), wn = pl.load_words(1), wr = pl.load_words(2), wi = pl.load_words(S - 1);
+  pl.rotate_stage(0, wc);
+  if (1 < npairs) pl.rotate_stage(1, wn);
+  asm volatile("s_barrier" ::: "memory");
+  f32x4 s[2][RB];
+  pl.scores(pl.stage(0), koff, qr, s);
 
   for (int p = 0; p < npairs; ++p) {
-    // copies issued after pair p: min(kStages - 2, npairs - 1 - p) stages
-    const int after = min(kStages - 2, npairs - 1 - p);
-    if (after >= 2)
-      wait_vmcnt<2 * SG::kLoads>();
-    else if (after == 1)
-      wait_vmcnt<SG::kLoads>();
-    else
-      wait_vmcnt<0>();
-    // Every wave has waited for its own copies of pair p; the barrier makes
-    // them complete for all waves and frees buffer (p - 1) % kStages.  A bare
-    // s_barrier (compiler memory clobber only): a fenced __syncthreads would
-    // also drain the copies of the later pairs still in flight.
+    // Own copies of pair p + 2 complete: at most the later pairs' copies
+    // (p + 3 .. p + S - 2) stay outstanding.
+    wait_stages<SG::kLoads, S - 4>(max(0, min(S - 4, npairs - 3 - p)));
+    // The barrier makes pair p + 2 complete for all waves, publishes the
+    // rotation of pair p + 1, and frees buffer (p - 1) % S (its V was read
+    // at iteration p - 1, its K at p - 2).  A bare s_barrier (compiler
+    // memory clobber only): a fenced __syncthreads would also drain the
+    // copies of the later pairs still in flight.
     asm volatile("s_barrier" ::: "memory");
-    if (p + kStages - 1 < npairs) pl.issue(p + kStages - 1);
-    if (!has_rows) continue;
+    // This pair's softmax and products first, then the copies and the
+    // rotation for later pairs: those run while the matrix cores drain the
+    // products just issued.
+    const PairWords wp = wc;
+    if (has_rows) {
+      const unsigned char* st = pl.stage(p);
+      TileMeta mt[2];
+      int delta[2];
+      bool priv[2];
+      pl.pair_meta(p, wp, mt, delta, priv);
 
-    const unsigned char* st = lds_buf + (p % kStages) * SG::kBytes;
-    TileMeta mt[2];
-    int delta[2];
-    bool priv[2];
-    pl.pair_meta(p, mt, delta, priv);
+      // V^T operand of channel block n: the 8 tokens this lane's scores hold
+      F8 vv[NV];
+#pragma unroll
+      for (int n = 0; n < NV; ++n) vv[n] = *reinterpret_cast<const F8*>(st + voff + n * 512);
 
-    // scores S^T[key 4g+j][row r] of both tiles, raw (unscaled)
-    f32x4 s[2][RB];
+      // Masking only where a slot can be invalid: partial or dropped tiles,
+      // causal private tiles, ALiBi bias (wave-uniform test on the words).
+      const bool full = KIND != kAlibi && (mt[0].mask & mt[1].mask) == 0xFFFFu && !priv[0] && !priv[1];
+      if (!full) {
+        const bool hi = g >= 2;
+        const uint32_t msk = hi ? mt[1].mask : mt[0].mask;
+        const int off = hi ? mt[1].offset : mt[0].offset;
+        const bool pv = hi ? priv[1] : priv[0];
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      if (P::kRot && delta[x] != cur_delta) {
-        pl.rotate(qr, raw, st, x, delta[x]);
-        cur_delta = delta[x];
-      }
-      F8 kf[NC];
-      const unsigned char* kt = st + SG::kK + x * SG::kTile + r * (DH * 2);
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        kf[c] = *reinterpret_cast<const F8*>(kt + (((4 * c + g) ^ (r % SG::kChunksPerRow)) << 4));
+          for (int j = 0; j < 4; ++j) {
+            const int tok = 8 * (g & 1) + 4 * h + j;
+            const bool filled = (msk >> tok) & 1u;
+            const int kpos = off + tok;
 #pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            for (int b = 0; b < RB; ++b) {
+              const bool ok = filled && (!pv || kpos <= qp[b]);
+              float v = s[h][b][j];
+              if (KIND == kAlibi) v = fmaf(slope_raw[b], (float)(kpos - qp[b]), v);
+              s[h][b][j] = ok ? v : -INFINITY;
+            }
+            // empty slots hold unwritten pool bytes: zero their V (p is 0 there)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[c], qr[b][c], z, 0, 0, 0);
-        s[x][b] = z;
-      }
-    }
-    // V^T operand of channel block n: slots 0..3 = tile 0 tokens 4g..4g+3,
-    // slots 4..7 = tile 1 tokens 4g..4g+3 (the keys this lane's scores hold)
-    F8 vv[NV];
-#pragma unroll
-    for (int n = 0; n < NV; ++n) {
-      const int off = (16 * n + r) * 32 + (((g >> 1) ^ ((r >> 3) & 1)) << 4) + ((g & 1) << 3);
-      const F4 lo = *reinterpret_cast<const F4*>(st + SG::kV + off);
-      const F4 hi = *reinterpret_cast<const F4*>(st + SG::kV + SG::kTile + off);
-      vv[n] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-
-    // Masking only where a slot can be invalid: partial or dropped tiles,
-    // causal private tiles, ALiBi bias (wave-uniform test on the words).
-    const bool full = KIND != kAlibi && (mt[0].mask & mt[1].mask) == 0xFFFFu && !priv[0] && !priv[1];
-    if (!full) {
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int slot = 4 * g + j;
-          const bool filled = (mt[x].mask >> slot) & 1u;
-          const int kpos = mt[x].offset + slot;
-#pragma unroll
-          for (int b = 0; b < RB; ++b) {
-            const bool ok = filled && (!priv[x] || kpos <= qp[b]);
-            float v = s[x][b][j];
-            if (KIND == kAlibi) v = fmaf(slope_raw[b], (float)(kpos - qp[b]), v);
-            s[x][b][j] = ok ? v : -INFINITY;
-          }
-          // empty slots hold unwritten pool bytes: zero their V (p is 0 there)
-          if (!filled) {
-#pragma unroll
-            for (int n = 0; n < NV; ++n) vv[n][4 * x + j] = (bf16)0.f;
+            for (int n = 0; n < NV; ++n) vv[n][4 * h + j] = filled ? vv[n][4 * h + j] : (bf16)0.f;
           }
         }
       }
-    }
 
-    // Lazy rescale: the reference max m_run only moves (and acc, l are
-    // rescaled) when some row's score exceeds it by more than 2^SLACK, so
-    // every weight stays <= 2^SLACK; exact in real arithmetic, and the combine
-    // uses the same reference.  Checked per lane on raw scores (scale > 0).
-    float mx[RB];
-    bool grow = false;
-#pragma unroll
-    for (int b = 0; b < RB; ++b) {
-      float m = fmaxf(s[0][b][0], s[0][b][1]);
-      m = fmaxf(m, fmaxf(s[0][b][2], s[0][b][3]));
-      m = fmaxf(m, fmaxf(s[1][b][0], s[1][b][1]));
-      m = fmaxf(m, fmaxf(s[1][b][2], s[1][b][3]));
-      mx[b] = m;
-      grow = grow || (m > thr[b]);
-    }
-    if (__any(grow)) {
+      // Lazy rescale: the reference max m_run only moves (and acc, l are
+      // rescaled) when some row's score exceeds it by more than 2^SLACK, so
+      // every weight stays <= 2^SLACK; exact in real arithmetic, and the combine
+      // uses the same reference.  Checked per lane on raw scores (scale > 0).
+      float mx[RB];
+      bool grow = false;
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
-        const float m_new = fmaxf(m_run[b], xor_max16_32(mx[b]) * sl);
-        const float alpha = (m_run[b] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[b] - m_new);
+        float m = fmaxf(fmaxf(s[0][b][0], s[0][b][1]), fmaxf(s[0][b][2], s[0][b][3]));
+        m = fmaxf(m, fmaxf(fmaxf(s[1][b][0], s[1][b][1]), fmaxf(s[1][b][2], s[1][b][3])));
+        mx[b] = m;
+        grow = grow || (m > thr[b]);
+      }
+      if (__any(grow)) {
 #pragma unroll
-        for (int n = 0; n < NV; ++n) acc[b][n] *= alpha;
-        lsum[b] *= alpha;
-        m_run[b] = m_new;
-        const bool none = m_new == -INFINITY;
-        negm[b] = none ? 0.f : -m_new;
-        thr[b] = none ? -INFINITY : (m_new + (float)LAZY_RESCALE_SLACK) / sl;
+        for (int b = 0; b < RB; ++b) {
+          const float m_new = fmaxf(m_run[b], xor_max16_32(mx[b]) * sl);
+          const float alpha = (m_run[b] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[b] - m_new);
+#pragma unroll
+          for (int n = 0; n < NV; ++n) acc[b][n] *= alpha;
+          lsum[b] *= alpha;
+          m_run[b] = m_new;
+          const bool none = m_new == -INFINITY;
+          negm[b] = none ? 0.f : -m_new;
+          thr[b] = none ? -INFINITY : (m_new + (float)LAZY_RESCALE_SLACK) / sl;
+        }
+      }
+
+      // weights p = 2^(s * scale_log2 - m_run), row sums and P V on the
+      // MFMAs, with the next pair's scores in the same straight-line block
+      // (their products overlap this pair's exponentials); past the last pair
+      // they are computed from a stale buffer and never used
+      F8 pf[RB];
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pf[b][4 * h + j] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[h][b][j], sl, negm[b]));
+      pl.scores(pl.stage(p + 1), koff, qr, s);
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[b], lsum[b], 0, 0, 0);
+#pragma unroll
+        for (int n = 0; n < NV; ++n) acc[b][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv[n], pf[b], acc[b][n], 0, 0, 0);
       }
     }
-
-    // weights p = 2^(s * scale_log2 - m_run), row sums and P V on the MFMAs
-#pragma unroll
-    for (int b = 0; b < RB; ++b) {
-      F8 pf;
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pf[4 * x + j] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[x][b][j], sl, negm[b]));
-      lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lsum[b], 0, 0, 0);
-#pragma unroll
-      for (int n = 0; n < NV; ++n) acc[b][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv[n], pf, acc[b][n], 0, 0, 0);
-    }
+    if (p + S - 1 < npairs) pl.issue(p + S - 1, wi);
+    if (p + 2 < npairs) pl.rotate_stage(p + 2, wr);
+    wc = wn;
+    wn = wr;
+    wr = pl.load_words(p + 3);
+    wi = pl.load_words(p + S);
   }
   if (!has_rows) return;
 
@@ -448,33 +557,30 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a) {
 
 namespace {
 
-template <int DH, int KIND, bool DEFER, int RB, int NW>
+template <int DH, int KIND, bool DEFER, int RB>
 hipError_t launch_rb(const AttnArgs& a, int row_tiles, int splits, int num_reqs, int hkv, hipStream_t st) {
+  constexpr int NW = kPrefillWaves;
   constexpr bool rot = (KIND != kAlibi) && DEFER;
-  const size_t lds = (size_t)kStages * StageGeom<DH, rot, NW>::kBytes + (size_t)NW * RB * (DH / 32) * 64 * 16;
+  using SG = StageGeom<DH, rot, NW>;
+  const size_t lds = (size_t)SG::kStages * SG::kBytes;
   static bool attr_set = false;  // the ring needs more than the default 64 KiB of dynamic LDS
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&prefill_lds_kernel<DH, KIND, DEFER, RB, NW>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_lds_kernel<DH, KIND, DEFER, RB, NW>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid((unsigned)(row_tiles * splits), (unsigned)hkv, (unsigned)num_reqs);
-  hipLaunchKernelGGL((prefill_lds_kernel<DH, KIND, DEFER, RB, NW>), grid, dim3(64 * NW), lds, st, a);
+  const int num_wgs = row_tiles * splits * hkv * num_reqs;  // 1-D: the kernel maps ids to units
+  hipLaunchKernelGGL((prefill_lds_kernel<DH, KIND, DEFER, RB, NW>), dim3((unsigned)num_wgs), dim3(64 * NW), lds, st, a,
+                     row_tiles, num_wgs);
   return hipGetLastError();
 }
 
-// rows per workgroup = 16 x rb x 4 (the host plan's row tile)
+// rows per workgroup = 16 x rb x 4 (the host plan's row tile) = 8 waves x (rb / 2) blocks
 template <int DH, int KIND, bool DEFER>
 hipError_t launch_kind(const AttnArgs& a, int rb, int row_tiles, int splits, int num_reqs, int hkv, hipStream_t st) {
-  constexpr int NW = LAZY_PREFILL_LDS_WAVES;
-  static_assert(NW == 4 || NW == 8, "waves per workgroup");
-  if (NW == 8)
-    return rb == 4 ? launch_rb<DH, KIND, DEFER, 2, NW>(a, row_tiles, splits, num_reqs, hkv, st)
-                   : launch_rb<DH, KIND, DEFER, 1, NW>(a, row_tiles, splits, num_reqs, hkv, st);
-  return rb == 4 ? launch_rb<DH, KIND, DEFER, 4, 4>(a, row_tiles, splits, num_reqs, hkv, st)
-                 : launch_rb<DH, KIND, DEFER, 2, 4>(a, row_tiles, splits, num_reqs, hkv, st);
+  return rb == 4 ? launch_rb<DH, KIND, DEFER, 2>(a, row_tiles, splits, num_reqs, hkv, st)
+                 : launch_rb<DH, KIND, DEFER, 1>(a, row_tiles, splits, num_reqs, hkv, st);
 }
 
 template <int DH>
