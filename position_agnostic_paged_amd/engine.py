@@ -55,10 +55,79 @@ class PosDesc:
         return c
 
 
-class TileTable:
-    """Device copy of the packed tile words of a batch of requests."""
+class StepUploads:
+    """Host metadata of one step (positions, slot ids, tile words, row starts)
+    packed into a pinned buffer and moved to the device with one copy.
 
-    def __init__(self, layouts: Sequence[RequestLayout], kind_id: int, num_blocks: int, device):
+    ``begin()`` starts a step, ``add(array)`` stages an array and returns its
+    index, ``commit()`` issues the single host-to-device copy on the current
+    stream and returns device views in ``add`` order (callbacks registered with
+    ``on_commit`` receive them too).  Two pinned buffers alternate, and a
+    buffer is refilled only after its previous copy has executed; the device
+    buffer is reused in stream order (the next copy runs after the kernels that
+    read the previous one)."""
+
+    ALIGN = 256
+
+    def __init__(self, device, capacity: int = 8 << 20):
+        self.device = torch.device(device)
+        self.cap = capacity
+        self.host = [torch.empty(capacity, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+        self.host_np = [h.numpy() for h in self.host]
+        self.dev = torch.empty(capacity, dtype=torch.uint8, device=self.device)
+        self.done: List[Optional[torch.cuda.Event]] = [None, None]
+        self.cur = 1
+        self.items: List[Tuple[int, np.dtype, Tuple[int, ...]]] = []
+        self.callbacks = []
+        self.off = 0
+
+    def begin(self) -> None:
+        self.cur ^= 1
+        if self.done[self.cur] is not None:
+            self.done[self.cur].synchronize()
+        self.items, self.callbacks, self.off = [], [], 0
+
+    def add(self, arr) -> int:
+        a = np.ascontiguousarray(arr)
+        if a.dtype == np.uint64:
+            a = a.view(np.int64)
+        off = (self.off + self.ALIGN - 1) // self.ALIGN * self.ALIGN
+        if off + a.nbytes > self.cap:
+            raise ValueError(f"step metadata exceeds {self.cap} bytes")
+        self.host_np[self.cur][off: off + a.nbytes] = a.reshape(-1).view(np.uint8)
+        self.items.append((off, a.dtype, a.shape))
+        self.off = off + a.nbytes
+        return len(self.items) - 1
+
+    def on_commit(self, fn) -> None:
+        self.callbacks.append(fn)
+
+    def commit(self) -> List[torch.Tensor]:
+        n = self.off
+        if n:
+            self.dev[:n].copy_(self.host[self.cur][:n], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.done[self.cur] = ev
+        views = []
+        for off, dt, shape in self.items:
+            tdt = TORCH_INT[np.dtype(dt)]
+            nb = int(np.prod(shape)) * np.dtype(dt).itemsize
+            views.append(self.dev[off: off + nb].view(tdt).view(shape))
+        for fn in self.callbacks:
+            fn(views)
+        return views
+
+
+TORCH_INT = {np.dtype(np.int32): torch.int32, np.dtype(np.int64): torch.int64, np.dtype(np.uint8): torch.uint8}
+
+
+class TileTable:
+    """Device copy of the packed tile words of a batch of requests (uploaded on
+    its own, or staged into a step's ``StepUploads``)."""
+
+    def __init__(self, layouts: Sequence[RequestLayout], kind_id: int, num_blocks: int, device,
+                 uploads: Optional[StepUploads] = None):
         f = flatten_layouts(layouts)
         cap = sum(blocks_for(n) for n in f["seg_len"]) or 1
         tiles, tstart, nctx = L.build_tiles(kind_id, f["seg_start"], f["seg_len"], f["seg_pos0"], f["seg_is_ctx"],
@@ -67,9 +136,16 @@ class TileTable:
         self.num_reqs = len(layouts)
         self.max_tiles = int(np.max(np.diff(tstart))) if len(layouts) else 0
         self.total_tiles = int(tstart[-1]) if len(layouts) else 0
-        self.tiles = torch.from_numpy(tiles.view(np.int64) if tiles.size else np.zeros(1, np.int64)).to(device)
-        self.tile_start = torch.from_numpy(tstart).to(device)
-        self.ctx_tiles = torch.from_numpy(nctx if nctx.size else np.zeros(1, np.int32)).to(device)
+        arrays = (tiles.view(np.int64) if tiles.size else np.zeros(1, np.int64), tstart,
+                  nctx if nctx.size else np.zeros(1, np.int32))
+        if uploads is None:
+            self.tiles, self.tile_start, self.ctx_tiles = (torch.from_numpy(a).to(device) for a in arrays)
+        else:
+            ids = [uploads.add(a) for a in arrays]
+            uploads.on_commit(lambda views: self._bind(views, ids))
+
+    def _bind(self, views, ids) -> None:
+        self.tiles, self.tile_start, self.ctx_tiles = (views[i] for i in ids)
 
 
 class Engine:
@@ -128,8 +204,8 @@ class Engine:
             self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return self._ws
 
-    def tile_table(self, layouts: Sequence[RequestLayout]) -> TileTable:
-        return TileTable(layouts, self.pos.kind_id, self.num_blocks, self.device)
+    def tile_table(self, layouts: Sequence[RequestLayout], uploads: Optional[StepUploads] = None) -> TileTable:
+        return TileTable(layouts, self.pos.kind_id, self.num_blocks, self.device, uploads)
 
     def prefill(self, tt: TileTable, q: torch.Tensor, q_start: torch.Tensor, q_pos0: torch.Tensor, max_q_len: int,
                 out: Optional[torch.Tensor] = None, pos: Optional[L.PosDescC] = None, stream=None) -> torch.Tensor:
