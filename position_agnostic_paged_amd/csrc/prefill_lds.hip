@@ -225,60 +225,81 @@ struct LdsPrefill {
     }
   }
 
-  // R_Delta applied in place to the context K rows of a landed pair: each
-  // thread takes 4 rotation pairs of one row (half-split: dims 4u..4u+3 with
-  // their partners dh/2 away; interleaved: dims 8u..8u+7).  Tiles with
-  // Delta = 0 (private tokens, a document at position 0, dropped tiles) are
-  // already at their global positions.
-  __device__ __forceinline__ void rotate_stage(int q, const PairWords& pw) const {
-    if (!kRot) return;
+  // R_Delta applied in place to the context K rows of a landed pair, in two
+  // halves so the LDS reads can be issued early and their latency hidden
+  // behind the matrix products: rot_load reads this thread's item, rot_store
+  // rotates (fp32) and writes it back.  Each thread takes at most one item:
+  // 4 rotation pairs of one row (half-split: dims 4u..4u+3 with their
+  // partners dh/2 away; interleaved: dims 8u..8u+7).  Tiles with Delta = 0
+  // (private tokens, a document at position 0, dropped tiles) are already at
+  // their global positions.
+  struct RotWork {
+    F8 v;  // half-split: [lo dims | hi dims]; interleaved: the 8 dims
+    f32x4 c, s;
+    uint32_t o_lo, o_hi;  // byte offsets (o_hi unused for interleaved)
+    bool on;
+  };
+
+  __device__ __forceinline__ RotWork rot_load(int q, const PairWords& pw) const {
+    static_assert(2 * SG::kRotItems <= NW * 64, "one rotation item per thread");
+    RotWork w;
+    w.on = false;
+    if (!kRot) return w;
     TileMeta mt[2];
     int delta[2];
     bool priv[2];
     pair_meta(q, pw, mt, delta, priv);
-    unsigned char* st = stage(q);
+    const int wbase = wave * 64;  // wave-uniform
+    if (wbase >= 2 * SG::kRotItems) return w;
+    const int x = wbase / SG::kRotItems;
+    if ((x ? delta[1] : delta[0]) == 0) return w;
+    w.on = true;
+    const int i = wbase % SG::kRotItems + lane;
+    const int t = i / (DH / 8), u = i % (DH / 8);
+    const uint32_t st = (uint32_t)(q % S) * SG::kBytes;
+    const float* cs = reinterpret_cast<const float*>(lds + st + SG::kCS) + x * DH;
+    const uint32_t row = st + SG::kK + x * SG::kTile + t * (DH * 2);
+    const int key = k_key<DH>(t, x);
+    w.c = *reinterpret_cast<const f32x4*>(cs + 4 * u);
+    w.s = *reinterpret_cast<const f32x4*>(cs + DH / 2 + 4 * u);
+    if (KIND == kHalf) {
+      w.o_lo = row + ((((4 * u) / 8) ^ key) << 4) + ((u & 1) << 3);
+      w.o_hi = row + ((((4 * u + DH / 2) / 8) ^ key) << 4) + ((u & 1) << 3);
+      const F4 lo = *reinterpret_cast<const F4*>(lds + w.o_lo), hi = *reinterpret_cast<const F4*>(lds + w.o_hi);
+      w.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      w.o_lo = row + ((u ^ key) << 4);
+      w.o_hi = 0;
+      w.v = *reinterpret_cast<const F8*>(lds + w.o_lo);
+    }
+    return w;
+  }
+
+  __device__ __forceinline__ void rot_store(const RotWork& w) const {
+    if (!w.on) return;
+    if (KIND == kHalf) {
+      F4 nlo, nhi;
 #pragma unroll
-    for (int it0 = 0; it0 < 2 * SG::kRotItems; it0 += NW * 64) {
-      const int wbase = it0 + wave * 64;  // wave-uniform
-      if (wbase >= 2 * SG::kRotItems) break;
-      const int x = wbase / SG::kRotItems;
-      if ((x ? delta[1] : delta[0]) == 0) continue;
-      const int i = wbase % SG::kRotItems + lane;
-      const int t = i / (DH / 8), u = i % (DH / 8);
-      const float* cs = reinterpret_cast<const float*>(st + SG::kCS) + x * DH;
-      unsigned char* row = st + SG::kK + x * SG::kTile + t * (DH * 2);
-      const int key = k_key<DH>(t, x);
-      if (KIND == kHalf) {
-        const f32x4 c = *reinterpret_cast<const f32x4*>(cs + 4 * u);
-        const f32x4 s = *reinterpret_cast<const f32x4*>(cs + DH / 2 + 4 * u);
-        F4* plo = reinterpret_cast<F4*>(row + ((((4 * u) / 8) ^ key) << 4) + ((u & 1) << 3));
-        F4* phi = reinterpret_cast<F4*>(row + ((((4 * u + DH / 2) / 8) ^ key) << 4) + ((u & 1) << 3));
-        const F4 lo = *plo, hi = *phi;
-        F4 nlo, nhi;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float x1 = (float)lo[k], x2 = (float)hi[k];
-          nlo[k] = (bf16)(x1 * c[k] - x2 * s[k]);
-          nhi[k] = (bf16)(x2 * c[k] + x1 * s[k]);
-        }
-        *plo = nlo;
-        *phi = nhi;
-      } else {
-        const f32x4 c = *reinterpret_cast<const f32x4*>(cs + 4 * u);
-        const f32x4 s = *reinterpret_cast<const f32x4*>(cs + DH / 2 + 4 * u);
-        F8* pv = reinterpret_cast<F8*>(row + ((u ^ key) << 4));
-        const F8 v = *pv;
-        F8 nv;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float x1 = (float)v[2 * k], x2 = (float)v[2 * k + 1];
-          nv[2 * k] = (bf16)(x1 * c[k] - x2 * s[k]);
-          nv[2 * k + 1] = (bf16)(x2 * c[k] + x1 * s[k]);
-        }
-        *pv = nv;
+      for (int k = 0; k < 4; ++k) {
+        const float x1 = (float)w.v[k], x2 = (float)w.v[4 + k];
+        nlo[k] = (bf16)(x1 * w.c[k] - x2 * w.s[k]);
+        nhi[k] = (bf16)(x2 * w.c[k] + x1 * w.s[k]);
       }
+      *reinterpret_cast<F4*>(lds + w.o_lo) = nlo;
+      *reinterpret_cast<F4*>(lds + w.o_hi) = nhi;
+    } else {
+      F8 nv;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x1 = (float)w.v[2 * k], x2 = (float)w.v[2 * k + 1];
+        nv[2 * k] = (bf16)(x1 * w.c[k] - x2 * w.s[k]);
+        nv[2 * k + 1] = (bf16)(x2 * w.c[k] + x1 * w.s[k]);
+      }
+      *reinterpret_cast<F8*>(lds + w.o_lo) = nv;
     }
   }
+
+  __device__ __forceinline__ void rotate_stage(int q, const PairWords& pw) const { rot_store(rot_load(q, pw)); }
 
   // Raw scores of a pair's two tiles (K rows at their global positions):
   // s[h][b][j] = score of query row r of block b against the key whose
@@ -423,10 +444,14 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
     // memory clobber only): a fenced __syncthreads would also drain the
     // copies of the later pairs still in flight.
     asm volatile("s_barrier" ::: "memory");
-    // This pair's softmax and products first, then the copies and the
-    // rotation for later pairs: those run while the matrix cores drain the
-    // products just issued.
+    // Rotation of pair p + 2 in two halves around this pair's softmax and
+    // products: its LDS reads now, its arithmetic and write-back (and the
+    // next copies) after the products are issued, while the matrix cores
+    // drain them.
     const PairWords wp = wc;
+    typename P::RotWork rot;
+    rot.on = false;
+    if (p + 2 < npairs) rot = pl.rot_load(p + 2, wr);
     if (has_rows) {
       const unsigned char* st = pl.stage(p);
       TileMeta mt[2];
@@ -515,8 +540,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
         for (int n = 0; n < NV; ++n) acc[b][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv[n], pf[b], acc[b][n], 0, 0, 0);
       }
     }
+    pl.rot_store(rot);  // rotation of pair p + 2 (its LDS reads were issued before the products)
     if (p + S - 1 < npairs) pl.issue(p + S - 1, wi);
-    if (p + 2 < npairs) pl.rotate_stage(p + 2, wr);
     wc = wn;
     wn = wr;
     wr = pl.load_words(p + 3);
