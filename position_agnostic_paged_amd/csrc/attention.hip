@@ -144,18 +144,29 @@ __global__ __launch_bounds__(64 * WT) void decode_kernel(AttnArgs a) {
 //   M = max_s m_s,  out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,
 // over the splits its request used.  Splits that saw no visible key carry
 // m = -inf and contribute nothing.
-template <typename T, int DH>
+template <typename T, int DH, int NG>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, T* __restrict__ out,
                                                       const int32_t* __restrict__ q_start,
                                                       const int32_t* __restrict__ tile_start, int32_t num_reqs,
                                                       int32_t hq, int32_t rows_bound, int32_t max_splits,
                                                       int32_t chunk) {
-  constexpr int TPR = DH / 4;  // threads per row, 4 channels each
-  const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-  const int c4 = (threadIdx.x % TPR) * 4;
+  // RPB rows per workgroup; per row, TPR threads cover the channels (4 each)
+  // and NG groups of them take every NG-th split, so the partial loads of
+  // many splits are in flight together (NG = 1 for few splits); the groups'
+  // maxima, weighted sums and vectors meet in LDS.
+  constexpr int TPR = DH / 4;
+  constexpr int RPB = 256 / (TPR * NG);
+  static_assert(RPB >= 1 && RPB * TPR * NG == 256, "combine shape");
+  __shared__ float red_m[RPB][NG], red_l[RPB][NG];
+  __shared__ f32x4 red_o[RPB][NG][TPR];
+  const int rr = threadIdx.x / (TPR * NG);
+  const int row = blockIdx.x * RPB + rr;
+  const int grp = (threadIdx.x / TPR) % NG;
+  const int ct = threadIdx.x % TPR;
+  const int c4 = ct * 4;
   const int rows = min(rows_bound, (q_start != nullptr) ? q_start[num_reqs] * hq : num_reqs * hq);
-  if (row >= rows) return;
+  if (row >= rows) return;  // uniform over the row's threads; barriers below only when NG > 1 (RPB = 1)
   int req;
   const int qrow = row / hq;
   if (q_start == nullptr) {
@@ -170,16 +181,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
   const int ns = request_splits(tile_start[req + 1] - tile_start[req], chunk, max_splits);
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[((int64_t)s * rows_bound + row) * 2]);
+  for (int s = grp; s < ns; s += NG) M = fmaxf(M, part_ml[((int64_t)s * rows_bound + row) * 2]);
+  if constexpr (NG > 1) {
+    if (ct == 0) red_m[rr][grp] = M;
+    __syncthreads();
+    M = red_m[rr][0];
+#pragma unroll
+    for (int i = 1; i < NG; ++i) M = fmaxf(M, red_m[rr][i]);
+  }
   const float Mu = (M == -INFINITY) ? 0.f : M;
   float L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ns; ++s) {
+  for (int s = grp; s < ns; s += NG) {
     const int64_t pr = (int64_t)s * rows_bound + row;
     const float w = __builtin_amdgcn_exp2f(part_ml[pr * 2] - Mu);
     L += w * part_ml[pr * 2 + 1];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + pr * DH + c4);
-    o += w * v;
+    o += w * *reinterpret_cast<const f32x4*>(part_o + pr * DH + c4);
+  }
+  if constexpr (NG > 1) {
+    red_o[rr][grp][ct] = o;
+    if (ct == 0) red_l[rr][grp] = L;
+    __syncthreads();
+    if (grp != 0) return;
+#pragma unroll
+    for (int i = 1; i < NG; ++i) {
+      o += red_o[rr][i][ct];
+      L += red_l[rr][i];
+    }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
   using F4 = typename Elem<T>::Frag4;
@@ -314,12 +342,20 @@ hipError_t dispatch_kind(int kind, bool defer, const AttnArgs& a, const Plan& p,
 
 template <typename T, int DH>
 hipError_t launch_combine(const AttnArgs& a, const Plan& p, const int32_t* q_start, int num_reqs, hipStream_t st) {
-  constexpr int rows_per_block = 256 / (DH / 4);
-  const int rows = p.rows_bound;
-  dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
-  hipLaunchKernelGGL((combine_kernel<T, DH>), grid, dim3(256), 0, st, a.part_o, a.part_ml,
-                     reinterpret_cast<T*>(a.out), q_start, a.tile_start, num_reqs, a.hq, p.rows_bound, p.splits,
-                     p.chunk);
+  // many splits: one row per workgroup, 256 / (DH/4) split groups; few: rows side by side
+  constexpr int NGMAX = 256 / (DH / 4);
+  if (p.splits > 4) {
+    dim3 grid((unsigned)p.rows_bound);
+    hipLaunchKernelGGL((combine_kernel<T, DH, NGMAX>), grid, dim3(256), 0, st, a.part_o, a.part_ml,
+                       reinterpret_cast<T*>(a.out), q_start, a.tile_start, num_reqs, a.hq, p.rows_bound, p.splits,
+                       p.chunk);
+  } else {
+    constexpr int RPB = NGMAX;
+    dim3 grid((unsigned)((p.rows_bound + RPB - 1) / RPB));
+    hipLaunchKernelGGL((combine_kernel<T, DH, 1>), grid, dim3(256), 0, st, a.part_o, a.part_ml,
+                       reinterpret_cast<T*>(a.out), q_start, a.tile_start, num_reqs, a.hq, p.rows_bound, p.splits,
+                       p.chunk);
+  }
   return hipGetLastError();
 }
 
