@@ -213,3 +213,16 @@ def test_attention_never_writes_the_cache():
     torch.cuda.synchronize()
     assert torch.equal(kb.view(torch.int16), eng.k_cache.view(torch.int16))
     assert torch.equal(vb.view(torch.int16), eng.v_cache.view(torch.int16))
+
+
+def test_falcon_alibi_prefill_mqa_dh64():
+    """ALiBi bias in the LDS-staged prefill: bf16, dh 64, MQA 71/1 (rows of one KV head span 14 row tiles)."""
+    _check_prefill("falcon7b_alibi_prefill")
+
+
+def test_dh64_interleaved_prefill_decode_and_control():
+    """dh 64 interleaved RoPE through the staged prefill (K rotated in LDS), the decode kernel and the
+    pre-rotated control on the no-sharing layout."""
+    _check_prefill("small_dh64_interleaved")
+    _check_prefill("small_dh64_interleaved", shared=False, prerotated=True)
+    _check_decode("small_dh64_interleaved", steps=[0, 1, 2, 3])

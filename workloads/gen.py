@@ -294,6 +294,55 @@ def _ragged() -> Workload:
     return wl
 
 
+def _falcon_alibi_prefill() -> Workload:
+    """Falcon-7B attention shape (MQA 71/1, dh 64, ALiBi) on a prefill batch: 4 requests x (5 Zipf docs
+    of 100..700 tokens + a question of 7..48 tokens)."""
+    wl = Workload(
+        name="falcon7b_mqa_alibi_prefill_b4",
+        wid=8,
+        geom=Geometry(71, 1, 64, "bf16"),
+        pos=PosSpec("alibi"),
+        kv_scale=0.5,
+        doc_lens={d: 100 + 37 * d for d in range(17)},
+        description="4 requests x (5 Zipf(1.3) docs of 100..692 tok from 17) + 7..48-token question; MQA 71 heads",
+    )
+    pre = []
+    for r, lq in enumerate([48, 7, 31, 16]):
+        pr = _question(wl, [r], lq, True)
+        pr.doc_ids = _zipf_pick(8, [r], 17, 5, 1.3)
+        pre.append(pr)
+    wl.prefill_steps = [pre]
+    return wl
+
+
+def _small_dh64_interleaved() -> Workload:
+    """dh 64 with interleaved RoPE and GQA 8/2 (bf16): a prefill batch and decode steps over documents
+    whose lengths leave partial last blocks."""
+    wl = Workload(
+        name="gqa8x2_d64_interleaved",
+        wid=9,
+        geom=Geometry(8, 2, 64, "bf16"),
+        pos=PosSpec("rope_interleaved", base=1e4),
+        kv_scale=0.5,
+        doc_lens={d: 37 + 61 * d for d in range(12)},
+        num_decode_steps=4,
+        description="3 prefills (4 docs of 37..708 tok + 20..60-tok question) and 5 decodes (2..6 docs)",
+    )
+    pre = []
+    for r, lq in enumerate([20, 60, 41]):
+        pr = _question(wl, [r], lq, True)
+        pr.doc_ids = _zipf_pick(9, [r], 12, 4, 1.0)
+        pre.append(pr)
+    wl.prefill_steps = [pre]
+    decs = []
+    for r, nd in enumerate([2, 6, 3, 5, 4]):
+        dr = _question(wl, [100 + r], 9 + r, False)
+        dr.doc_ids = _zipf_pick(9, [100 + r], 12, nd, 1.0)
+        decs.append(dr)
+    wl.decode_reqs = decs
+    return wl
+
+
 WORKLOADS = {
     "ragged": _ragged,
     "tiny_fp32": _tiny_fp32,
@@ -301,6 +350,8 @@ WORKLOADS = {
     "llama8b_decode": _decode_llama8b,
     "llama70b_mixed": _mixed_llama70b,
     "falcon7b_alibi": _falcon_alibi,
+    "falcon7b_alibi_prefill": _falcon_alibi_prefill,
+    "small_dh64_interleaved": _small_dh64_interleaved,
     "llama8b_prefill_interleaved": lambda: _prefill_llama8b(
         "rope_interleaved", 2, "llama8b_prefill_b8_10x200_interleaved"
     ),
