@@ -198,12 +198,16 @@ class DecodeScenario(_Base):
     def positions(self, step: int) -> np.ndarray:
         return (self.priv_pos0 + self.pre_len + step).astype(np.int32)
 
+    def slots(self, step: int) -> np.ndarray:
+        """Slot id of each request's new token at a step."""
+        return np.array([self.eng.slots_for(self.priv[r], 1, int(self.pre_len[r]) + step)[0] for r in range(self.R)],
+                        np.int64)
+
     def stage_inputs(self, step: int):
         """Device copies of the step's raw q/k/v, positions and slots (setup, not timed)."""
         q, k, v = self.wl.decode_step(step)
         pos = self.positions(step)
-        slots = np.array([self.eng.slots_for(self.priv[r], 1, int(self.pre_len[r]) + step)[0] for r in range(self.R)],
-                         np.int64)
+        slots = self.slots(step)
         t = (_to_dev(q, self.tdtype, self.dev), _to_dev(k, self.tdtype, self.dev), _to_dev(v, self.tdtype, self.dev),
              torch.from_numpy(pos).to(self.dev), torch.from_numpy(slots).to(self.dev))
         self._inputs[step] = t
@@ -221,6 +225,17 @@ class DecodeScenario(_Base):
             events[0].record()
         out = self.eng.decode(tt, self.q, pos, out=self.out, pos=self.eng.pos.with_flags(self.prerotated),
                               stream=stream)
+        if events is not None:
+            events[1].record()
+        return out
+
+    def attend(self, step: int, q: torch.Tensor, q_pos: torch.Tensor, stream=None, events=None) -> torch.Tensor:
+        """The attention call of a step alone, for a caller that wrote the new tokens itself (q already
+        rotated to its global position, q_pos on the device)."""
+        tt = self.tables[step] if self.tables is not None else self.table(step)
+        if events is not None:
+            events[0].record()
+        out = self.eng.decode(tt, q, q_pos, out=self.out, pos=self.eng.pos.with_flags(self.prerotated), stream=stream)
         if events is not None:
             events[1].record()
         return out
