@@ -32,7 +32,11 @@
 
 namespace lazy {
 
-constexpr int kPrefillWaves = 8;         // waves per workgroup: two per SIMD
+#ifndef LAZY_PREFILL_WAVES
+#define LAZY_PREFILL_WAVES 8  // waves per workgroup: 8 = two per SIMD, 2 x 16 rows each (4 = one per SIMD,
+                              // 4 x 16 rows: spills at dh 128, the rescale keeps the accumulators in VGPRs)
+#endif
+constexpr int kPrefillWaves = LAZY_PREFILL_WAVES;
 constexpr int kLdsBytes = 160 * 1024;    // LDS of one CU, all of it for the ring
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
@@ -227,75 +231,87 @@ struct LdsPrefill {
 
   // R_Delta applied in place to the context K rows of a landed pair, in two
   // halves so the LDS reads can be issued early and their latency hidden
-  // behind the matrix products: rot_load reads this thread's item, rot_store
-  // rotates (fp32) and writes it back.  Each thread takes at most one item:
-  // 4 rotation pairs of one row (half-split: dims 4u..4u+3 with their
-  // partners dh/2 away; interleaved: dims 8u..8u+7).  Tiles with Delta = 0
-  // (private tokens, a document at position 0, dropped tiles) are already at
-  // their global positions.
-  struct RotWork {
+  // behind the matrix products: rot_load reads this thread's items, rot_store
+  // rotates them (fp32) and writes them back.  An item is 4 rotation pairs of
+  // one row (half-split: dims 4u..4u+3 with their partners dh/2 away;
+  // interleaved: dims 8u..8u+7); a pair of tiles has 4 dh items over the
+  // workgroup's threads.  Tiles with Delta = 0 (private tokens, a document at
+  // position 0, dropped tiles) are already at their global positions.
+  static constexpr int kRI = (2 * SG::kRotItems + NW * 64 - 1) / (NW * 64);  // items per thread
+  struct RotItem {
     F8 v;  // half-split: [lo dims | hi dims]; interleaved: the 8 dims
     f32x4 c, s;
     uint32_t o_lo, o_hi;  // byte offsets (o_hi unused for interleaved)
     bool on;
   };
+  struct RotWork {
+    RotItem it[kRI];
+  };
 
   __device__ __forceinline__ RotWork rot_load(int q, const PairWords& pw) const {
-    static_assert(2 * SG::kRotItems <= NW * 64, "one rotation item per thread");
-    RotWork w;
-    w.on = false;
-    if (!kRot) return w;
+    RotWork rw;
+#pragma unroll
+    for (int k = 0; k < kRI; ++k) rw.it[k].on = false;
+    if (!kRot) return rw;
     TileMeta mt[2];
     int delta[2];
     bool priv[2];
     pair_meta(q, pw, mt, delta, priv);
-    const int wbase = wave * 64;  // wave-uniform
-    if (wbase >= 2 * SG::kRotItems) return w;
-    const int x = wbase / SG::kRotItems;
-    if ((x ? delta[1] : delta[0]) == 0) return w;
-    w.on = true;
-    const int i = wbase % SG::kRotItems + lane;
-    const int t = i / (DH / 8), u = i % (DH / 8);
     const uint32_t st = (uint32_t)(q % S) * SG::kBytes;
-    const float* cs = reinterpret_cast<const float*>(lds + st + SG::kCS) + x * DH;
-    const uint32_t row = st + SG::kK + x * SG::kTile + t * (DH * 2);
-    const int key = k_key<DH>(t, x);
-    w.c = *reinterpret_cast<const f32x4*>(cs + 4 * u);
-    w.s = *reinterpret_cast<const f32x4*>(cs + DH / 2 + 4 * u);
-    if (KIND == kHalf) {
-      w.o_lo = row + ((((4 * u) / 8) ^ key) << 4) + ((u & 1) << 3);
-      w.o_hi = row + ((((4 * u + DH / 2) / 8) ^ key) << 4) + ((u & 1) << 3);
-      const F4 lo = *reinterpret_cast<const F4*>(lds + w.o_lo), hi = *reinterpret_cast<const F4*>(lds + w.o_hi);
-      w.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    } else {
-      w.o_lo = row + ((u ^ key) << 4);
-      w.o_hi = 0;
-      w.v = *reinterpret_cast<const F8*>(lds + w.o_lo);
+#pragma unroll
+    for (int k = 0; k < kRI; ++k) {
+      RotItem& w = rw.it[k];
+      const int wbase = (k * NW + wave) * 64;  // wave-uniform
+      if (wbase >= 2 * SG::kRotItems) continue;
+      const int x = wbase / SG::kRotItems;
+      if ((x ? delta[1] : delta[0]) == 0) continue;
+      w.on = true;
+      const int i = wbase % SG::kRotItems + lane;
+      const int t = i / (DH / 8), u = i % (DH / 8);
+      const float* cs = reinterpret_cast<const float*>(lds + st + SG::kCS) + x * DH;
+      const uint32_t row = st + SG::kK + x * SG::kTile + t * (DH * 2);
+      const int key = k_key<DH>(t, x);
+      w.c = *reinterpret_cast<const f32x4*>(cs + 4 * u);
+      w.s = *reinterpret_cast<const f32x4*>(cs + DH / 2 + 4 * u);
+      if (KIND == kHalf) {
+        w.o_lo = row + ((((4 * u) / 8) ^ key) << 4) + ((u & 1) << 3);
+        w.o_hi = row + ((((4 * u + DH / 2) / 8) ^ key) << 4) + ((u & 1) << 3);
+        const F4 lo = *reinterpret_cast<const F4*>(lds + w.o_lo), hi = *reinterpret_cast<const F4*>(lds + w.o_hi);
+        w.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {
+        w.o_lo = row + ((u ^ key) << 4);
+        w.o_hi = 0;
+        w.v = *reinterpret_cast<const F8*>(lds + w.o_lo);
+      }
     }
-    return w;
+    return rw;
   }
 
-  __device__ __forceinline__ void rot_store(const RotWork& w) const {
-    if (!w.on) return;
-    if (KIND == kHalf) {
-      F4 nlo, nhi;
+  __device__ __forceinline__ void rot_store(const RotWork& rw) const {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x1 = (float)w.v[k], x2 = (float)w.v[4 + k];
-        nlo[k] = (bf16)(x1 * w.c[k] - x2 * w.s[k]);
-        nhi[k] = (bf16)(x2 * w.c[k] + x1 * w.s[k]);
-      }
-      *reinterpret_cast<F4*>(lds + w.o_lo) = nlo;
-      *reinterpret_cast<F4*>(lds + w.o_hi) = nhi;
-    } else {
-      F8 nv;
+    for (int k = 0; k < kRI; ++k) {
+      const RotItem& w = rw.it[k];
+      if (!w.on) continue;
+      if (KIND == kHalf) {
+        F4 nlo, nhi;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float x1 = (float)w.v[2 * k], x2 = (float)w.v[2 * k + 1];
-        nv[2 * k] = (bf16)(x1 * w.c[k] - x2 * w.s[k]);
-        nv[2 * k + 1] = (bf16)(x2 * w.c[k] + x1 * w.s[k]);
+        for (int j = 0; j < 4; ++j) {
+          const float x1 = (float)w.v[j], x2 = (float)w.v[4 + j];
+          nlo[j] = (bf16)(x1 * w.c[j] - x2 * w.s[j]);
+          nhi[j] = (bf16)(x2 * w.c[j] + x1 * w.s[j]);
+        }
+        *reinterpret_cast<F4*>(lds + w.o_lo) = nlo;
+        *reinterpret_cast<F4*>(lds + w.o_hi) = nhi;
+      } else {
+        F8 nv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x1 = (float)w.v[2 * j], x2 = (float)w.v[2 * j + 1];
+          nv[2 * j] = (bf16)(x1 * w.c[j] - x2 * w.s[j]);
+          nv[2 * j + 1] = (bf16)(x2 * w.c[j] + x1 * w.s[j]);
+        }
+        *reinterpret_cast<F8*>(lds + w.o_lo) = nv;
       }
-      *reinterpret_cast<F8*>(lds + w.o_lo) = nv;
     }
   }
 
@@ -450,7 +466,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
     // drain them.
     const PairWords wp = wc;
     typename P::RotWork rot;
-    rot.on = false;
+#pragma unroll
+    for (int k = 0; k < P::kRI; ++k) rot.it[k].on = false;
     if (p + 2 < npairs) rot = pl.rot_load(p + 2, wr);
     if (has_rows) {
       const unsigned char* st = pl.stage(p);
@@ -601,11 +618,13 @@ hipError_t launch_rb(const AttnArgs& a, int row_tiles, int splits, int num_reqs,
   return hipGetLastError();
 }
 
-// rows per workgroup = 16 x rb x 4 (the host plan's row tile) = 8 waves x (rb / 2) blocks
+// rows per workgroup = 16 x rb x 4 (the host plan's row tile) = NW waves x (4 rb / NW) blocks
 template <int DH, int KIND, bool DEFER>
 hipError_t launch_kind(const AttnArgs& a, int rb, int row_tiles, int splits, int num_reqs, int hkv, hipStream_t st) {
-  return rb == 4 ? launch_rb<DH, KIND, DEFER, 2>(a, row_tiles, splits, num_reqs, hkv, st)
-                 : launch_rb<DH, KIND, DEFER, 1>(a, row_tiles, splits, num_reqs, hkv, st);
+  constexpr int NW = kPrefillWaves;
+  static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  return rb == 4 ? launch_rb<DH, KIND, DEFER, 16 / NW>(a, row_tiles, splits, num_reqs, hkv, st)
+                 : launch_rb<DH, KIND, DEFER, 8 / NW>(a, row_tiles, splits, num_reqs, hkv, st);
 }
 
 template <int DH>
