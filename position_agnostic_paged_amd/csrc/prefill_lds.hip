@@ -460,15 +460,23 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
     // memory clobber only): a fenced __syncthreads would also drain the
     // copies of the later pairs still in flight.
     asm volatile("s_barrier" ::: "memory");
-    // Rotation of pair p + 2 in two halves around this pair's softmax and
-    // products: its LDS reads now, its arithmetic and write-back (and the
-    // next copies) after the products are issued, while the matrix cores
-    // drain them.
+    // Rotation of pair p + 2 in two halves: its LDS reads now, its
+    // arithmetic and write-back (with the next copies) in the other half of
+    // the iteration from this pair's softmax and products.
     const PairWords wp = wc;
     typename P::RotWork rot;
 #pragma unroll
     for (int k = 0; k < P::kRI; ++k) rot.it[k].on = false;
     if (p + 2 < npairs) rot = pl.rot_load(p + 2, wr);
+    // The two waves of a SIMD take the iteration's halves in opposite
+    // orders: waves 0..3 the softmax and products first, then the rotation
+    // and copies; waves 4..7 the other way round.  Each wave's matrix-heavy
+    // half then overlaps the other's vector and LDS half.
+    const bool copy_first = wave >= NW / 2;
+    if (copy_first) {
+      pl.rot_store(rot);  // rotation of pair p + 2
+      if (p + S - 1 < npairs) pl.issue(p + S - 1, wi);
+    }
     if (has_rows) {
       const unsigned char* st = pl.stage(p);
       TileMeta mt[2];
@@ -557,8 +565,10 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
         for (int n = 0; n < NV; ++n) acc[b][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv[n], pf[b], acc[b][n], 0, 0, 0);
       }
     }
-    pl.rot_store(rot);  // rotation of pair p + 2 (its LDS reads were issued before the products)
-    if (p + S - 1 < npairs) pl.issue(p + S - 1, wi);
+    if (!copy_first) {
+      pl.rot_store(rot);  // rotation of pair p + 2 (its LDS reads were issued before the products)
+      if (p + S - 1 < npairs) pl.issue(p + S - 1, wi);
+    }
     wc = wn;
     wn = wr;
     wr = pl.load_words(p + 3);
