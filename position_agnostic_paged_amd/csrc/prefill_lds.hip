@@ -67,7 +67,8 @@ struct StageGeom {
   static constexpr int kK = 0;                       // two K tiles
   static constexpr int kV = 2 * kTile;               // two V tiles
   static constexpr int kCS = 4 * kTile;              // two cos/sin rows (fp32 [dh])
-  static constexpr int kBytes = 4 * kTile + (ROT ? 2 * DH * 4 : 0);
+  static constexpr int kHdr = kCS + (ROT ? 2 * DH * 4 : 0);  // the pair's decoded tile words (PairHdr)
+  static constexpr int kBytes = kHdr + 32;
   static constexpr int kKChunks = 2 * kTile / 16;    // 16-B chunks of the K pair (same for V)
   static constexpr int kCopies = 2 * kKChunks / (NW * 64);  // K + V copies per thread
   static constexpr int kLoads = kCopies + (ROT ? 1 : 0);    // copies per wave per stage
@@ -88,6 +89,19 @@ typedef const __attribute__((address_space(4))) uint64_t* const_words;
 struct PairWords {
   uint64_t w0, w1;
 };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A pair's tile words decoded once, when its copies are issued, and kept in
+// its stage buffer for the rotation and the softmax: 32 bytes,
+//   [0] mask0 | mask1 << 16 (after the guards: a dropped tile has mask 0)
+//   [1] [2] the two tiles' word offsets (token position of the first slot)
+//   [3] bit 0 / 1: tile 0 / 1 is private; bit 2: both tiles full document tiles
+//   [4] [5] the rotation offsets Delta (0 where nothing is rotated)
+// Every wave would otherwise decode each pair three times on the CU's one
+// scalar unit.
+constexpr uint32_t kHdrPriv0 = 1u, kHdrPriv1 = 2u, kHdrFull = 4u;
 
 // K row swizzle: the 16-byte chunk q of row t of tile x sits at chunk
 // position q ^ key; tile 1 uses keys disjoint from tile 0's for the rows one
@@ -227,6 +241,24 @@ struct LdsPrefill {
         __builtin_amdgcn_global_load_lds(src, st + SG::kCS, 16, 0, 0);
       }
     }
+    // the decoded words for the later stages of this pair (one lane writes;
+    // read after at least three more barriers)
+    if (wave == 0 && lane == 0) {
+      const bool full = KIND != kAlibi && (mt[0].mask & mt[1].mask) == 0xFFFFu && !priv[0] && !priv[1];
+      const u32x4 h = {mt[0].mask | (mt[1].mask << 16), (uint32_t)mt[0].offset, (uint32_t)mt[1].offset,
+                       (priv[0] ? kHdrPriv0 : 0u) | (priv[1] ? kHdrPriv1 : 0u) | (full ? kHdrFull : 0u)};
+      const u32x2 d = {(uint32_t)delta[0], (uint32_t)delta[1]};
+      *reinterpret_cast<u32x4*>(st + SG::kHdr) = h;
+      *reinterpret_cast<u32x2*>(st + SG::kHdr + 16) = d;
+    }
+  }
+
+  // the header words of pair q (broadcast LDS reads; made uniform by the caller)
+  __device__ __forceinline__ u32x4 read_hdr(int q) const {
+    return *reinterpret_cast<const u32x4*>(stage(q) + SG::kHdr);
+  }
+  __device__ __forceinline__ u32x2 read_deltas(int q) const {
+    return *reinterpret_cast<const u32x2*>(stage(q) + SG::kHdr + 16);
   }
 
   // R_Delta applied in place to the context K rows of a landed pair, in two
@@ -248,15 +280,11 @@ struct LdsPrefill {
     RotItem it[kRI];
   };
 
-  __device__ __forceinline__ RotWork rot_load(int q, const PairWords& pw) const {
+  __device__ __forceinline__ RotWork rot_load(int q, const int (&delta)[2]) const {
     RotWork rw;
 #pragma unroll
     for (int k = 0; k < kRI; ++k) rw.it[k].on = false;
     if (!kRot) return rw;
-    TileMeta mt[2];
-    int delta[2];
-    bool priv[2];
-    pair_meta(q, pw, mt, delta, priv);
     const uint32_t st = (uint32_t)(q % S) * SG::kBytes;
 #pragma unroll
     for (int k = 0; k < kRI; ++k) {
@@ -315,7 +343,11 @@ struct LdsPrefill {
     }
   }
 
-  __device__ __forceinline__ void rotate_stage(int q, const PairWords& pw) const { rot_store(rot_load(q, pw)); }
+  __device__ __forceinline__ void rotate_stage(int q) const {
+    const u32x2 d = read_deltas(q);
+    const int delta[2] = {uniform((int)d[0]), uniform((int)d[1])};
+    rot_store(rot_load(q, delta));
+  }
 
   // Raw scores of a pair's two tiles (K rows at their global positions):
   // s[h][b][j] = score of query row r of block b against the key whose
@@ -440,12 +472,23 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
     if (q < npairs) pl.issue(q, pl.load_words(q));
   wait_stages<SG::kLoads, S - 3>(min(S - 3, npairs - 2));
   asm volatile("s_barrier" ::: "memory");
-  // Tile words travel through scalar registers: pair p (consumed), p + 2
-  // (rotated) and p + S - 1 (copied) at iteration p, each read one
-  // iteration ahead.
-  PairWords wc = pl.load_words(0), wn = pl.load_words(1), wr = pl.load_words(2), wi = pl.load_words(S - 1);
-  pl.rotate_stage(0, wc);
-  if (1 < npairs) pl.rotate_stage(1, wn);
+  // Tile words of the pair to copy next travel through scalar registers, read
+  // one iteration ahead; the later stages use the pair's decoded header,
+  // likewise read one iteration ahead (pair p + 1 for the softmax, p + 3 for
+  // the rotation).
+  PairWords wi = pl.load_words(S - 1);
+  pl.rotate_stage(0);
+  if (1 < npairs) pl.rotate_stage(1);
+  u32x4 hc;
+  int dr[2];
+  {
+    const u32x4 h = pl.read_hdr(0);
+    const u32x2 d = pl.read_deltas(2);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) hc[k] = (uint32_t)uniform((int)h[k]);
+    dr[0] = uniform((int)d[0]);
+    dr[1] = uniform((int)d[1]);
+  }
   asm volatile("s_barrier" ::: "memory");
   f32x4 s[2][RB];
   pl.scores(pl.stage(0), koff, qr, s);
@@ -463,11 +506,13 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
     // Rotation of pair p + 2 in two halves: its LDS reads now, its
     // arithmetic and write-back (with the next copies) in the other half of
     // the iteration from this pair's softmax and products.
-    const PairWords wp = wc;
+    // headers for the next iteration (written at least three barriers ago)
+    const u32x4 hv_next = pl.read_hdr(p + 1);
+    const u32x2 dv_next = pl.read_deltas(p + 3);
     typename P::RotWork rot;
 #pragma unroll
     for (int k = 0; k < P::kRI; ++k) rot.it[k].on = false;
-    if (p + 2 < npairs) rot = pl.rot_load(p + 2, wr);
+    if (p + 2 < npairs) rot = pl.rot_load(p + 2, dr);
     // The two waves of a SIMD take the iteration's halves in opposite
     // orders: waves 0..3 the softmax and products first, then the rotation
     // and copies; waves 4..7 the other way round.  Each wave's matrix-heavy
@@ -479,10 +524,6 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
     }
     if (has_rows) {
       const unsigned char* st = pl.stage(p);
-      TileMeta mt[2];
-      int delta[2];
-      bool priv[2];
-      pl.pair_meta(p, wp, mt, delta, priv);
 
       // V^T operand of channel block n: the 8 tokens this lane's scores hold
       F8 vv[NV];
@@ -491,12 +532,12 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
 
       // Masking only where a slot can be invalid: partial or dropped tiles,
       // causal private tiles, ALiBi bias (wave-uniform test on the words).
-      const bool full = KIND != kAlibi && (mt[0].mask & mt[1].mask) == 0xFFFFu && !priv[0] && !priv[1];
+      const bool full = (hc[3] & kHdrFull) != 0u;
       if (!full) {
         const bool hi = g >= 2;
-        const uint32_t msk = hi ? mt[1].mask : mt[0].mask;
-        const int off = hi ? mt[1].offset : mt[0].offset;
-        const bool pv = hi ? priv[1] : priv[0];
+        const uint32_t msk = hi ? (hc[0] >> 16) : (hc[0] & 0xFFFFu);
+        const int off = (int)(hi ? hc[2] : hc[1]);
+        const bool pv = (hc[3] & (hi ? kHdrPriv1 : kHdrPriv0)) != 0u;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -569,10 +610,11 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
       pl.rot_store(rot);  // rotation of pair p + 2 (its LDS reads were issued before the products)
       if (p + S - 1 < npairs) pl.issue(p + S - 1, wi);
     }
-    wc = wn;
-    wn = wr;
-    wr = pl.load_words(p + 3);
     wi = pl.load_words(p + S);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) hc[k] = (uint32_t)uniform((int)hv_next[k]);
+    dr[0] = uniform((int)dv_next[0]);
+    dr[1] = uniform((int)dv_next[1]);
   }
   if (!has_rows) return;
 
