@@ -503,12 +503,12 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
     // memory clobber only): a fenced __syncthreads would also drain the
     // copies of the later pairs still in flight.
     asm volatile("s_barrier" ::: "memory");
-    // Rotation of pair p + 2 in two halves: its LDS reads now, its
-    // arithmetic and write-back (with the next copies) in the other half of
-    // the iteration from this pair's softmax and products.
     // headers for the next iteration (written at least three barriers ago)
     const u32x4 hv_next = pl.read_hdr(p + 1);
     const u32x2 dv_next = pl.read_deltas(p + 3);
+    // Rotation of pair p + 2 in two halves: its LDS reads now, its
+    // arithmetic and write-back (with the next copies) in the other half of
+    // the iteration from this pair's softmax and products.
     typename P::RotWork rot;
 #pragma unroll
     for (int k = 0; k < P::kRI; ++k) rot.it[k].on = false;
