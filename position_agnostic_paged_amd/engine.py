@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 from . import lazy_attn as L
-from .paging import BlockPool, DocCache, RequestLayout, blocks_for, flatten_layouts
+from .paging import BlockPool, DocCache, RequestLayout, Segment, blocks_for, flatten_layouts
 
 TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
 
@@ -195,6 +195,64 @@ class Engine:
             k, v = content_fn()
             self.write_segment(blocks, k, v, 0)
         return blocks, hit
+
+    def process_documents(self, items: Sequence[Tuple[int, torch.Tensor, torch.Tensor, torch.Tensor]],
+                          out: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, List[List[int]]]:
+        """The pass that runs on a document miss: write each document's
+        position-agnostic cache entry and compute its own (block-diagonal,
+        causal) attention, both at local positions 0..L-1.
+
+        ``items`` = [(doc_id, k [L][Hkv][dh], v [L][Hkv][dh], q [L][Hq][dh])]
+        of documents not yet cached.  One kv-write stores every document's
+        K/V at its local positions (the copy later requests reuse at any
+        offset) and rotates the queries in place; one prefill then treats
+        each document as a request with no cached context whose own tokens
+        are its causal suffix starting at position 0 -- for a document at
+        offset 0 local and global positions coincide (LazyAttention notes,
+        "Method: overall framework": a document is encoded once, on its
+        first use, and reused position-agnostically afterwards).  ``q`` is
+        overwritten with the rotated queries.  Returns the outputs
+        ([sum L][Hq][dh], documents in order) and each document's blocks;
+        the documents stay pinned until released."""
+        if not items:
+            raise ValueError("process_documents needs at least one document")
+        ids = [int(it[0]) for it in items]
+        lens = [int(it[1].shape[0]) for it in items]
+        for (doc_id, k, v, q), n in zip(items, lens):
+            if n < 1 or v.shape[0] != n or q.shape[0] != n:
+                raise ValueError(f"document {doc_id}: k, v and q must have the same positive length")
+            if doc_id in self.docs:
+                raise ValueError(f"document {doc_id} is already cached: it has no miss to process")
+        if len(set(ids)) != len(ids):
+            raise ValueError("process_documents: a document appears twice")
+        blocks_all, layouts, pos, slots = [], [], [], []
+        try:
+            for doc_id, n in zip(ids, lens):
+                blocks, _ = self.docs.acquire(doc_id, n)
+                blocks_all.append(blocks)
+                layouts.append(RequestLayout([Segment(blocks, n, 0, False)]))
+                pos.append(np.arange(n, dtype=np.int32))
+                slots.append(self.slots_for(blocks, n))
+            K = torch.cat([it[1] for it in items]).contiguous()
+            V = torch.cat([it[2] for it in items]).contiguous()
+            Q = torch.cat([it[3] for it in items]).contiguous()
+            self.kv_write(K, V, Q, torch.from_numpy(np.concatenate(pos)).to(self.device),
+                          torch.from_numpy(np.concatenate(slots)).to(self.device), stream=stream)
+            tt = self.tile_table(layouts)
+            q_start = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device=self.device)
+            q_pos0 = torch.zeros(len(items), dtype=torch.int32, device=self.device)
+            o = self.prefill(tt, Q, q_start, q_pos0, max(lens), out=out, stream=stream)
+        except Exception:
+            # nothing half-written stays in the cache
+            for doc_id in ids[: len(blocks_all)]:
+                self.docs.forget(doc_id)
+            raise
+        # the rotated queries go back to the callers' tensors
+        off = 0
+        for (_, _, _, q), n in zip(items, lens):
+            q.copy_(Q[off: off + n])
+            off += n
+        return o, blocks_all
 
     # ----------------------------------------------------------- attention
     def _workspace(self, nbytes: int) -> Optional[torch.Tensor]:

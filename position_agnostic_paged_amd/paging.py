@@ -103,6 +103,12 @@ class DocCache:
             raise ValueError(f"doc {doc_id} is not pinned")
         d.pins -= 1
 
+    def forget(self, doc_id: int) -> None:
+        """Drop a document whatever its pins (a miss whose content was never written)."""
+        d = self._docs.pop(doc_id)
+        self.pool.free(d.blocks)
+        self.used -= len(d.blocks)
+
     def _make_room(self, need: int) -> None:
         def room() -> int:
             return min(self.budget - self.used, self.pool.free_blocks)

@@ -55,3 +55,13 @@ def test_layout_places_documents_consecutively():
     lay = layout_request([([1, 2], 20), ([3], 5)], [9], 3)
     assert [(s.pos0, s.length, s.ctx) for s in lay.segments] == [(0, 20, True), (20, 5, True), (25, 3, False)]
     assert lay.length == 28 and lay.num_tiles == 4
+
+
+def test_forget_drops_an_unwritten_miss_and_returns_its_blocks():
+    c = DocCache(BlockPool(8))
+    blocks, hit = c.acquire(5, 40)  # a miss, pinned, content not yet written
+    assert not hit and c.used == 3 and c.pool.free_blocks == 5
+    c.forget(5)
+    assert 5 not in c and c.used == 0 and c.pool.free_blocks == 8
+    b2, hit2 = c.acquire(5, 40)  # asked again: a miss again, not a hit on unwritten blocks
+    assert not hit2 and sorted(b2) == sorted(blocks)

@@ -9,6 +9,9 @@ of draw:
     2  suffix (question) q/k/v (per request)
     3  decode-step q/k/v (per step)
     4  lengths (mixed-batch decode context sizes)
+    5  queries of a document's own tokens (the document-processing pass
+       that writes its cache entry on a miss; per document id), and extra
+       question draws keyed by a caller-chosen id
 
 so any single document, request or step can be regenerated on its own.  Draws
 are fp32 normals; bf16 workloads round them to the nearest bf16 (ties to even)
@@ -110,6 +113,18 @@ class Workload:
         if cache:
             self._doc_cache[doc_id] = kv
         return kv
+
+    def doc_queries(self, doc_id: int) -> np.ndarray:
+        """Raw queries [L][Hq][dh] of a document's own tokens (its processing pass on a miss)."""
+        g = self.geom
+        return self._normal([5, 0, doc_id], (self.doc_lens[doc_id], g.num_q_heads, g.head_dim), 1.0)
+
+    def extra_question(self, key: int, length: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """A question (q [L][Hq][dh], k, v [L][Hkv][dh]) outside the workload's own requests."""
+        g = self.geom
+        q = self._normal([5, 1, key], (length, g.num_q_heads, g.head_dim), 1.0)
+        kv = self._normal([5, 2, key], (2, length, g.num_kv_heads, g.head_dim), self.kv_scale)
+        return q, kv[0], kv[1]
 
     def decode_step(self, step: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
         """q [R][Hq][dh], k [R][Hkv][dh], v [R][Hkv][dh] raw draws for every decode request at one step."""
