@@ -44,14 +44,15 @@ def _check_prefill(key, shared=True, prerotated=False, on_the_fly=False):
     assert err <= TOL[wl.geom.dtype]
 
 
-def _check_decode(key, steps, reqs=None, shared=True, prerotated=False, num_steps=None):
+def _check_decode(key, steps, reqs=None, shared=True, prerotated=False, num_steps=None, on_the_fly=False):
     from position_agnostic_paged_amd.scenarios import DecodeScenario
 
     wl = make_workload(key)
     if num_steps is not None:
         wl.num_decode_steps = num_steps
-    say(f"[decode parity] {wl.name} steps={list(steps)} shared={shared} prerotated={prerotated}")
-    eng = _engine(wl, shared)
+    say(f"[decode parity] {wl.name} steps={list(steps)} shared={shared} prerotated={prerotated} "
+        f"on_the_fly={on_the_fly}")
+    eng = _engine(wl, shared, on_the_fly=on_the_fly)
     sc = DecodeScenario(wl, eng, shared=shared, prerotated=prerotated)
     R = sc.R
     reqs = list(range(R)) if reqs is None else list(reqs)
@@ -122,6 +123,17 @@ def test_ragged_decode_uneven_splits():
 
 def test_llama8b_prefill_on_the_fly_sincos():
     _check_prefill("llama8b_prefill", on_the_fly=True)
+
+
+@pytest.mark.parametrize("on_the_fly", [False, True], ids=["table", "on_the_fly"])
+def test_long_context_offsets_beyond_100k(on_the_fly):
+    """128K-token contexts, base 1e4: document offsets up to ~128K (angles ~1.3e5 rad) through the
+    fp32 table and through the in-kernel fp64-reduced sincos, 8023 tiles in one request (offsets past
+    2^16 in the tile words, many splits).  The attention output averages over so many keys that it
+    cannot see a small angle error; the rotation itself is checked element by element at these
+    positions in test_rotation_gpu."""
+    _check_prefill("long_context", on_the_fly=on_the_fly)
+    _check_decode("long_context", steps=[0, 1], on_the_fly=on_the_fly)
 
 
 def test_mixed_yarn_prefill_step0():

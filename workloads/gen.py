@@ -358,8 +358,35 @@ def _small_dh64_interleaved() -> Workload:
     return wl
 
 
+def _long_context() -> Workload:
+    """Documents far from position 0: eight of 15.7K-16.4K tokens and one of 5 tokens, 128K tokens in all,
+    RoPE base 1e4 (rotation angles up to ~1.3e5 rad, where the table and the in-kernel sincos must stay
+    exact): one prefill with an 8-token question after every document (the 5-token one last) and two
+    decode requests over the documents in other orders."""
+    wl = Workload(
+        name="long_ctx128k_h2kv1_d128",
+        wid=10,
+        geom=Geometry(2, 1, 128, "bf16"),
+        pos=PosSpec("rope_half", base=1e4),
+        kv_scale=0.5,
+        doc_lens={**{d: 16384 - 97 * d for d in range(8)}, 8: 5},
+        num_decode_steps=2,
+        description="9 documents (8 x ~16K + 5 tok) = 128,361 tokens; 1 prefill (8-tok question), 2 decodes; GQA 2/1",
+    )
+    pr = _question(wl, [0], 8, True)
+    pr.doc_ids = [3, 0, 6, 1, 7, 2, 5, 4, 8]
+    wl.prefill_steps = [[pr]]
+    d0 = _question(wl, [100], 3, False)
+    d0.doc_ids = [8, 7, 6, 5, 4, 3, 2, 1, 0]
+    d1 = _question(wl, [101], 0, False)
+    d1.doc_ids = list(range(9))
+    wl.decode_reqs = [d0, d1]
+    return wl
+
+
 WORKLOADS = {
     "ragged": _ragged,
+    "long_context": _long_context,
     "tiny_fp32": _tiny_fp32,
     "llama8b_prefill": lambda: _prefill_llama8b("rope_half", 2, "llama8b_prefill_b8_10x200"),
     "llama8b_decode": _decode_llama8b,
