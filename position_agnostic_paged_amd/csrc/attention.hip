@@ -180,33 +180,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     req = lo;
   }
   const int ns = request_splits(tile_start[req + 1] - tile_start[req], chunk, max_splits);
-  float M = -INFINITY;
-  for (int s = grp; s < ns; s += NG) M = fmaxf(M, part_ml[((int64_t)s * rows_bound + row) * 2]);
-  if constexpr (NG > 1) {
-    if (ct == 0) red_m[rr][grp] = M;
-    __syncthreads();
-    M = red_m[rr][0];
-#pragma unroll
-    for (int i = 1; i < NG; ++i) M = fmaxf(M, red_m[rr][i]);
-  }
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f;
+  // One pass: each group merges its splits into a running (m, l, o),
+  // rescaling when the maximum grows, so every partial load is independent
+  // of the others (an empty split, m = -inf, has weight 0).
+  float M = -INFINITY, L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   for (int s = grp; s < ns; s += NG) {
     const int64_t pr = (int64_t)s * rows_bound + row;
-    const float w = __builtin_amdgcn_exp2f(part_ml[pr * 2] - Mu);
-    L += w * part_ml[pr * 2 + 1];
-    o += w * *reinterpret_cast<const f32x4*>(part_o + pr * DH + c4);
+    const float ms = part_ml[pr * 2], ls = part_ml[pr * 2 + 1];
+    const f32x4 os = *reinterpret_cast<const f32x4*>(part_o + pr * DH + c4);
+    const float mn = fmaxf(M, ms);
+    const float a = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+    const float b = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - mn);
+    o = o * a + os * b;
+    L = L * a + ls * b;
+    M = mn;
   }
   if constexpr (NG > 1) {
+    if (ct == 0) {
+      red_m[rr][grp] = M;
+      red_l[rr][grp] = L;
+    }
     red_o[rr][grp][ct] = o;
-    if (ct == 0) red_l[rr][grp] = L;
     __syncthreads();
     if (grp != 0) return;
+    float Mt = red_m[rr][0];
 #pragma unroll
-    for (int i = 1; i < NG; ++i) {
-      o += red_o[rr][i][ct];
-      L += red_l[rr][i];
+    for (int i = 1; i < NG; ++i) Mt = fmaxf(Mt, red_m[rr][i]);
+    o = f32x4{0.f, 0.f, 0.f, 0.f};
+    L = 0.f;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const float mi = red_m[rr][i];
+      const float w = (mi == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mi - Mt);
+      o += w * red_o[rr][i][ct];
+      L += w * red_l[rr][i];
     }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
