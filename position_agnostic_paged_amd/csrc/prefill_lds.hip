@@ -27,7 +27,13 @@
 //     reduction and the rescale only run when some row's maximum grows by
 //     more than 2^LAZY_RESCALE_SLACK; the scale folds into the exponent's
 //     FMA; row sums come from one extra MFMA against a ones operand (the
-//     sum of exactly the bf16 weights that multiply V).
+//     sum of exactly the bf16 weights that multiply V);
+//   * a pair's two tile words are decoded once, when its copies are issued,
+//     into a small header in its stage buffer (the CU's one scalar unit
+//     serves all eight waves);
+//   * the two waves sharing a SIMD take each iteration's halves in opposite
+//     orders, so one's matrix products overlap the other's vector, scalar
+//     and LDS work between the same two barriers.
 #include "attn_common.hpp"
 
 namespace lazy {
