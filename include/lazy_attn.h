@@ -100,7 +100,8 @@ typedef struct {
 typedef struct {
   int32_t kind;          /* lazy_pos_kind */
   uint32_t flags;        /* LAZY_FLAG_* */
-  int32_t max_pos;       /* rows of cos_sin; every rotation position must be < max_pos */
+  int32_t max_pos;       /* rows of cos_sin: every rotation position must be < max_pos (unused when
+                            cos_sin is NULL: the in-kernel sincos takes any position < 2^24) */
   float softmax_scale;   /* logit multiplier, e.g. 1/sqrt(dh) (x YaRN temperature gain) */
   const float* cos_sin;  /* device [max_pos][dh]; NULL selects on-the-fly sincos from inv_freq */
   const double* inv_freq;    /* device [dh/2] theta_k; used only when cos_sin == NULL */
@@ -172,8 +173,9 @@ lazy_status lazy_build_tiles(int32_t kind, int32_t num_reqs, const int32_t* seg_
  * [T][Hq][dh] (nullable, updated in place); positions int32 [T];
  * slot_mapping int64 [T].  A token whose slot is negative is not written to
  * the cache (its q is still rotated).  Device-side guards: a slot >=
- * num_blocks*16, or a RoPE position outside [0, max_pos), skips that token
- * (no cache write, q untouched) -- callers must pass valid values.
+ * num_blocks*16, a negative RoPE position, or (with a cos/sin table) a
+ * position >= max_pos skips that token (no cache write, q untouched) --
+ * callers must pass valid values.
  * Rotation math is fp32; stored values are rounded once to T. */
 lazy_status lazy_kv_write(const lazy_geom* geom, const lazy_pos_desc* pos, void* k_cache, void* v_cache,
                           int64_t num_blocks, const void* k, const void* v, void* q_inout,

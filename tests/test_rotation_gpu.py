@@ -1,4 +1,4 @@
-"""GPU: the rotation itself, element by element, at positions up to 2^17 - 1.
+"""GPU: the rotation itself, element by element, at positions up to 2^17 - 1 (2^24 - 1 in-kernel).
 
 Attention outputs are too forgiving to see a small angle error (a wrong
 angle in one high-frequency pair moves a softmax-weighted average by far
@@ -6,7 +6,8 @@ less than the bf16 tolerance), so the rotation is checked where it is
 applied: ``lazy_kv_write`` on fp32 keys and queries at positions spread over
 [0, 131072) writes R_p k into the cache and R_p q in place, through the
 fp64-built fp32 table and through the in-kernel sincos (fp64 angle with
-exact reduction, fp32 sincos).  Both must match the oracle's fp64 rotation
+exact reduction, fp32 sincos; also at positions up to 2^24 - 1, the largest
+offset a tile word carries).  Both must match the oracle's fp64 rotation
 to within fp32 rounding; an angle formed in fp32 (an error near 4e-3 rad at
 p ~ 1.3e5 for the pair of frequency 1) would miss by three orders of
 magnitude.  The V cache must hold v unrotated, in the channel-major layout.
@@ -23,6 +24,7 @@ from workloads.gen import PosSpec
 pytestmark = pytest.mark.gpu
 
 MAX_POS = 1 << 17
+LIMIT = 1 << 24  # positions a tile word's 24-bit offset field can hold
 N = 4096  # tokens, one slot each
 
 
@@ -47,6 +49,12 @@ def test_kv_write_rotation_at_large_positions(case, on_the_fly):
     rng = np.random.default_rng(11)
     p = rng.choice(MAX_POS, size=N, replace=False).astype(np.int32)
     p[:4] = [0, 1, MAX_POS - 1, MAX_POS - 2]
+    if on_the_fly:
+        # no table bounds the in-kernel sincos: half the tokens go up to the largest offset a tile
+        # word can carry (2^24 - 1), where the angle of the frequency-1 pair is ~1.7e7 rad
+        far = rng.choice(np.arange(MAX_POS, LIMIT), size=N // 2, replace=False).astype(np.int32)
+        p[N // 2:] = far
+        p[-1] = LIMIT - 1
     k = rng.standard_normal((N, hkv, dh)).astype(np.float32) * 2.0
     v = rng.standard_normal((N, hkv, dh)).astype(np.float32)
     q = rng.standard_normal((N, hq, dh)).astype(np.float32)
