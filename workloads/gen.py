@@ -384,8 +384,47 @@ def _long_context() -> Workload:
     return wl
 
 
+def _pages_overhead() -> Workload:
+    """The shape of the pages' overhead experiment (LazyAttention notes, "Ablation / kernel overhead"):
+    five 4096-token documents and a 64-token question per request, three documents hot (shared by
+    every request, in a per-request order) and two cold (private to the request); Llama-3.1-8B
+    attention shape.  4 prefill requests and 64 decode requests (4 decode steps)."""
+    n_pre, n_dec = 4, 64
+    hot = [0, 1, 2]
+    wl = Workload(
+        name="pages_overhead_5x4096_q64_llama8b",
+        wid=11,
+        geom=Geometry(32, 8, 128, "bf16"),
+        pos=PosSpec("rope_half", base=5e5),
+        kv_scale=0.5,
+        doc_lens={d: 4096 for d in range(3 + 2 * (n_pre + n_dec))},
+        num_decode_steps=4,
+        description="5 x 4096-tok docs (3 hot, 2 private) + 64-tok question; 4 prefills, 64 decodes",
+    )
+
+    def docs_for(k: int, r: int) -> List[int]:
+        rng = np.random.default_rng(np.random.SeedSequence([11, 1, k]))
+        cold = [3 + 2 * r, 4 + 2 * r]
+        return [int(d) for d in rng.permutation(hot + cold)]
+
+    pre = []
+    for r in range(n_pre):
+        pr = _question(wl, [r], 64, True)
+        pr.doc_ids = docs_for(r, r)
+        pre.append(pr)
+    wl.prefill_steps = [pre]
+    decs = []
+    for r in range(n_dec):
+        dr = _question(wl, [100 + r], 64, False)
+        dr.doc_ids = docs_for(100 + r, n_pre + r)
+        decs.append(dr)
+    wl.decode_reqs = decs
+    return wl
+
+
 WORKLOADS = {
     "ragged": _ragged,
+    "pages_overhead": _pages_overhead,
     "long_context": _long_context,
     "tiny_fp32": _tiny_fp32,
     "llama8b_prefill": lambda: _prefill_llama8b("rope_half", 2, "llama8b_prefill_b8_10x200"),
