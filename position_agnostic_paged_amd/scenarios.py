@@ -231,9 +231,10 @@ class DecodeScenario(_Base):
 
     def attend(self, step: int, q: torch.Tensor, q_pos: torch.Tensor, stream=None, events=None) -> torch.Tensor:
         """The attention call of a step alone, for a caller that wrote the new tokens itself (q already
-        rotated to its global position, q_pos on the device)."""
+        rotated to its global position, q_pos on the device).  ``events[0]`` may be None when the
+        caller's previous end event already marks the start."""
         tt = self.tables[step] if self.tables is not None else self.table(step)
-        if events is not None:
+        if events is not None and events[0] is not None:
             events[0].record()
         out = self.eng.decode(tt, q, q_pos, out=self.out, pos=self.eng.pos.with_flags(self.prerotated), stream=stream)
         if events is not None:

@@ -31,3 +31,26 @@ def test_step_uploads_round_trip_and_tile_table():
         ref = TileTable(layouts, L.KIND_BY_NAME["rope_half"], 64, "cuda")
         for x, y in ((tt.tiles, ref.tiles), (tt.tile_start, ref.tile_start), (tt.ctx_tiles, ref.ctx_tiles)):
             assert torch.equal(x.cpu(), y.cpu())
+
+
+def test_step_uploads_overlap_never_overwrites_a_buffer_in_use():
+    """Commits back to back with no host synchronisation while the compute
+    stream lags behind (a spinning kernel before each read): every step's
+    device views must still hold that step's data when its kernels run, even
+    though the copies of later steps run on their own stream."""
+    from position_agnostic_paged_amd.engine import StepUploads
+
+    rng = np.random.default_rng(5)
+    up = StepUploads("cuda", capacity=1 << 20)
+    want, got = [], []
+    for step in range(8):
+        up.begin()
+        a = rng.integers(-2**31, 2**31 - 1, size=4096, dtype=np.int64).astype(np.int32)
+        ia = up.add(a)
+        views = up.commit()
+        torch.cuda._sleep(2_000_000)  # the compute stream falls behind the copies
+        got.append(views[ia].clone())  # read on the compute stream, in stream order
+        want.append(a)
+    torch.cuda.synchronize()
+    for a, g in zip(want, got):
+        assert np.array_equal(g.cpu().numpy(), a)
