@@ -544,12 +544,15 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
         const uint32_t msk = hi ? (hc[0] >> 16) : (hc[0] & 0xFFFFu);
         const int off = (int)(hi ? hc[2] : hc[1]);
         const bool pv = (hc[3] & (hi ? kHdrPriv1 : kHdrPriv0)) != 0u;
+        // fill bits of this lane's eight tokens 8 (g % 2) + t (t = the slot in
+        // its score and V fragments)
+        const uint32_t m8 = (msk >> (8 * (g & 1))) & 0xFFu;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int tok = 8 * (g & 1) + 4 * h + j;
-            const bool filled = (msk >> tok) & 1u;
+            const bool filled = (m8 >> (4 * h + j)) & 1u;
             const int kpos = off + tok;
 #pragma unroll
             for (int b = 0; b < RB; ++b) {
@@ -558,11 +561,17 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
               if (KIND == kAlibi) v = fmaf(slope_raw[b], (float)(kpos - qp[b]), v);
               s[h][b][j] = ok ? v : -INFINITY;
             }
-            // empty slots hold unwritten pool bytes: zero their V (p is 0 there)
-#pragma unroll
-            for (int n = 0; n < NV; ++n) vv[n][4 * h + j] = filled ? vv[n][4 * h + j] : (bf16)0.f;
           }
         }
+        // Empty slots hold unwritten pool bytes: zero their V (their weight is
+        // 0, but 0 x NaN is not).  Every channel block of the lane has the same
+        // eight slots, so one AND mask per dword (two bf16 slots) covers all.
+        u32x4 dm;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          dm[d] = (((m8 >> (2 * d)) & 1u) ? 0x0000FFFFu : 0u) | (((m8 >> (2 * d + 1)) & 1u) ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int n = 0; n < NV; ++n) vv[n] = __builtin_bit_cast(F8, __builtin_bit_cast(u32x4, vv[n]) & dm);
       }
 
       // Lazy rescale: the reference max m_run only moves (and acc, l are
