@@ -182,7 +182,18 @@ struct LdsPrefill {
     }
   }
 
-  __device__ __forceinline__ unsigned char* stage(int q) const { return lds + (q % S) * SG::kBytes; }
+  // Stage buffers are addressed relative to the buffer of pair base_q, whose
+  // byte offset base_off the loop keeps in one scalar register: pair q
+  // (base_q <= q < base_q + S) sits kBytes (q - base_q) further on, wrapped
+  // once.  A modulo per use would be strength-reduced by the compiler into
+  // two terms, each added to every per-lane LDS address.
+  uint32_t base_off = 0;
+  int base_q = 0;
+  __device__ __forceinline__ uint32_t stage_off(int q) const {
+    const uint32_t o = base_off + (uint32_t)(q - base_q) * SG::kBytes;
+    return o >= (uint32_t)(S * SG::kBytes) ? o - (uint32_t)(S * SG::kBytes) : o;
+  }
+  __device__ __forceinline__ unsigned char* stage(int q) const { return lds + stage_off(q); }
 
   __device__ __forceinline__ PairWords load_words(int q) const {
     PairWords pw{0ull, 0ull};
@@ -291,7 +302,7 @@ struct LdsPrefill {
 #pragma unroll
     for (int k = 0; k < kRI; ++k) rw.it[k].on = false;
     if (!kRot) return rw;
-    const uint32_t st = (uint32_t)(q % S) * SG::kBytes;
+    const uint32_t st = stage_off(q);
 #pragma unroll
     for (int k = 0; k < kRI; ++k) {
       RotItem& w = rw.it[k];
@@ -499,7 +510,11 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
   f32x4 s[2][RB];
   pl.scores(pl.stage(0), koff, qr, s);
 
+  uint32_t sp = 0;  // byte offset of pair p's stage buffer
   for (int p = 0; p < npairs; ++p) {
+    asm volatile("" : "+s"(sp));  // one opaque scalar (see stage_off)
+    pl.base_q = p;
+    pl.base_off = sp;
     // Own copies of pair p + 2 complete: at most the later pairs' copies
     // (p + 3 .. p + S - 2) stay outstanding.
     wait_stages<SG::kLoads, S - 4>(max(0, min(S - 4, npairs - 3 - p)));
@@ -630,6 +645,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
     for (int k = 0; k < 4; ++k) hc[k] = (uint32_t)uniform((int)hv_next[k]);
     dr[0] = uniform((int)dv_next[0]);
     dr[1] = uniform((int)dv_next[1]);
+    sp = pl.stage_off(p + 1);
   }
   if (!has_rows) return;
 
