@@ -28,6 +28,9 @@
 //     more than 2^LAZY_RESCALE_SLACK; the scale folds into the exponent's
 //     FMA; row sums come from one extra MFMA against a ones operand (the
 //     sum of exactly the bf16 weights that multiply V);
+//   * the wave raises its issue priority over its run of P V products, so
+//     they go out back to back while the other wave of the SIMD fills the
+//     matrix core's shadow with vector work;
 //   * a pair's two tile words are decoded once, when its copies are issued,
 //     into a small header in its stage buffer (the CU's one scalar unit
 //     serves all eight waves);
@@ -629,12 +632,14 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
 #pragma unroll
           for (int j = 0; j < 4; ++j) pf[b][4 * h + j] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[h][b][j], sl, negm[b]));
       pl.scores(pl.stage(p + 1), koff, qr, s);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
         lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[b], lsum[b], 0, 0, 0);
 #pragma unroll
         for (int n = 0; n < NV; ++n) acc[b][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv[n], pf[b], acc[b][n], 0, 0, 0);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     if (!copy_first) {
       pl.rot_store(rot);  // rotation of pair p + 2 (its LDS reads were issued before the products)
