@@ -61,7 +61,7 @@ def lib() -> C.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run `python -m position_agnostic_paged_amd.build`")
         L = C.CDLL(LIB_PATH)
-        P, I32, I64, U32 = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32
+        P, I32, I64 = C.c_void_p, C.c_int32, C.c_int64
         sig = {
             "lazy_rope_freqs": [I32, C.c_double, C.c_double, I32, C.c_double, C.c_double, P, P],
             "lazy_rope_table": [I32, P, I32, P],
@@ -82,7 +82,6 @@ def lib() -> C.CDLL:
         L.lazy_attn_workspace_size.restype = C.c_size_t
         L.lazy_last_error.argtypes = []
         L.lazy_last_error.restype = C.c_char_p
-        _ = U32
         _lib = L
     return _lib
 
