@@ -147,7 +147,12 @@ lazy_status lazy_unpack_tiles(const uint64_t* words, int64_t n, int64_t* block_i
  * its first token sits at global position seg_pos0[s].  seg_is_ctx[s] = 1
  * marks a cached document written at local positions (a context segment);
  * 0 marks private tokens written at global positions.  Context segments
- * must precede private ones within a request.
+ * must precede private ones within a request; among themselves they may come
+ * in any order (every tile carries its own offset, and the attention result
+ * does not depend on key order beyond rounding).  Listing a batch's shared
+ * documents in one common order, most shared first, lets the decode read a
+ * shared document for all its requests at about the same time, so that the
+ * reads after the first come from L2.
  *
  * Outputs (host, caller-allocated): tiles_out[tiles_cap] words,
  * tile_start[num_reqs+1] (tile range of request r), ctx_tiles[num_reqs]

@@ -82,10 +82,14 @@ __global__ __launch_bounds__(64 * WR) void prefill_kernel(AttnArgs a) {
 // Decode: one wave = the G query heads of one (request, KV head) x one split;
 // a workgroup = WT waves on WT consecutive splits.  Software-pipelined: the
 // next pair's K/V loads are in flight while the current pair is consumed.
-// The KV head is the grid's fastest dimension: dispatch deals consecutive
-// workgroups round-robin over the 8 XCDs, so with 8 KV heads every XCD (its
-// own L2) serves one head, and all requests that read a shared document's
-// block read that head's slice through the same L2.
+// Grid (KV head, request, split group), fastest first.  Dispatch deals
+// consecutive workgroups round-robin over the 8 XCDs, so with 8 KV heads
+// every XCD (its own L2) serves one head, and all requests that read a shared
+// document's block read that head's slice through the same L2.  Split groups
+// are the slowest dimension, so the first splits of every request run
+// together: with the host listing each request's documents most shared
+// first, a shared document is read for all its requests at about the same
+// time and mostly comes from L2 after the first read.
 template <typename T, int DH, int KIND, bool DEFER, int RB, int WT>
 __global__ __launch_bounds__(64 * WT) void decode_kernel(AttnArgs a) {
   using W = WaveAttn<T, DH, KIND, DEFER, false, RB>;
@@ -95,9 +99,9 @@ __global__ __launch_bounds__(64 * WT) void decode_kernel(AttnArgs a) {
 #else
   const int wt = threadIdx.x >> 6;
 #endif
-  const int req = blockIdx.z;
+  const int req = blockIdx.y;
   const int kvh = blockIdx.x;
-  const int split = blockIdx.y * WT + wt;
+  const int split = blockIdx.z * WT + wt;
   const int nt = a.tile_start[req + 1] - a.tile_start[req];
   int sb, se;
   if (!split_range(nt, a.chunk, a.num_splits, split, sb, se)) return;  // unused split (no barriers follow)
@@ -305,7 +309,7 @@ size_t ws_bytes_for(const lazy_geom* g, const Plan& p) {
 
 template <typename T, int DH, int KIND, bool DEFER, int RB>
 hipError_t launch_decode(const AttnArgs& a, const Plan& p, int num_reqs, int hkv, hipStream_t st) {
-  dim3 grid((unsigned)hkv, (unsigned)((p.splits + kDecodeWT - 1) / kDecodeWT), (unsigned)num_reqs);
+  dim3 grid((unsigned)hkv, (unsigned)num_reqs, (unsigned)((p.splits + kDecodeWT - 1) / kDecodeWT));
   hipLaunchKernelGGL((decode_kernel<T, DH, KIND, DEFER, RB, kDecodeWT>), grid, dim3(64 * kDecodeWT), 0, st, a);
   return hipGetLastError();
 }

@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 from . import lazy_attn as L
-from .paging import BlockPool, DocCache, RequestLayout, Segment, blocks_for, flatten_layouts
+from .paging import BlockPool, DocCache, RequestLayout, Segment, blocks_for, flatten_layouts, order_for_reuse
 
 TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
 
@@ -262,7 +262,12 @@ class Engine:
             self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return self._ws
 
+    # list each request's cached documents most shared first (paging.order_for_reuse)
+    order_for_reuse = True
+
     def tile_table(self, layouts: Sequence[RequestLayout], uploads: Optional[StepUploads] = None) -> TileTable:
+        if self.order_for_reuse:
+            layouts = order_for_reuse(layouts)
         return TileTable(layouts, self.pos.kind_id, self.num_blocks, self.device, uploads)
 
     def prefill(self, tt: TileTable, q: torch.Tensor, q_start: torch.Tensor, q_pos0: torch.Tensor, max_q_len: int,

@@ -179,6 +179,33 @@ def layout_request(doc_blocks: Sequence[Tuple[List[int], int]], private_blocks: 
     return RequestLayout(segs)
 
 
+def order_for_reuse(layouts: Sequence[RequestLayout]) -> List[RequestLayout]:
+    """The same requests with each one's cached documents listed most shared first.
+
+    A cached document is the same blocks in every request that reads it, so
+    its first block names it.  Listing every request's documents by how many
+    requests of the batch read them (then by that block) puts a shared
+    document at about the same tile index everywhere: the split-K kernels
+    then read it for all those requests at about the same time, and the
+    copies after the first come from the cache hierarchy.  Each tile carries
+    its own offset and the softmax does not depend on key order, so only the
+    rounding order of the sums changes.  Private tokens stay after the
+    documents, where the kernels expect them.
+    """
+    count: Dict[int, int] = {}
+    for lay in layouts:
+        for sg in lay.segments:
+            if sg.ctx and sg.blocks:
+                count[sg.blocks[0]] = count.get(sg.blocks[0], 0) + 1
+    out = []
+    for lay in layouts:
+        docs = [sg for sg in lay.segments if sg.ctx and sg.blocks]
+        rest = [sg for sg in lay.segments if not (sg.ctx and sg.blocks)]
+        docs.sort(key=lambda sg: (-count[sg.blocks[0]], sg.blocks[0]))
+        out.append(RequestLayout(docs + rest))
+    return out
+
+
 def flatten_layouts(layouts: Sequence[RequestLayout]) -> Dict[str, list]:
     """Segment arrays in the form lazy_build_tiles takes."""
     seg_start, seg_len, seg_pos0, seg_ctx, seg_bstart, blocks = [0], [], [], [], [0], []

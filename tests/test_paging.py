@@ -3,7 +3,8 @@ documents, private blocks charged to the same budget) and request layouts."""
 
 import pytest
 
-from position_agnostic_paged_amd.paging import BlockPool, CacheFull, DocCache, blocks_for, layout_request
+from position_agnostic_paged_amd.paging import (BlockPool, CacheFull, DocCache, RequestLayout, Segment, blocks_for,
+                                                layout_request, order_for_reuse)
 
 
 def test_blocks_for():
@@ -65,3 +66,29 @@ def test_forget_drops_an_unwritten_miss_and_returns_its_blocks():
     assert 5 not in c and c.used == 0 and c.pool.free_blocks == 8
     b2, hit2 = c.acquire(5, 40)  # asked again: a miss again, not a hit on unwritten blocks
     assert not hit2 and sorted(b2) == sorted(blocks)
+
+
+def test_order_for_reuse_lists_shared_documents_first_and_keeps_everything():
+    """Each request keeps exactly its segments (offsets attached), private tokens stay last, and the
+    documents go most shared first, ties by first block: a shared document gets the same rank in
+    every request that reads it."""
+    a, b = Segment([10, 11], 20, 0, True), Segment([3], 7, 0, True)
+    c, d = Segment([40], 16, 0, True), Segment([7], 5, 0, True)
+
+    def at(sg, pos):
+        return Segment(sg.blocks, sg.length, pos, True)
+
+    lays = [
+        RequestLayout([at(c, 0), at(a, 16), at(b, 36), Segment([90], 3, 43, False)]),
+        RequestLayout([at(b, 0), at(d, 7), at(a, 12), Segment([91, 92], 17, 32, False)]),
+        RequestLayout([at(a, 0), at(c, 20), Segment([93], 1, 36, False)]),
+        RequestLayout([Segment([94], 4, 0, False)]),
+    ]
+    out = order_for_reuse(lays)
+    # a: 3 requests, b: 2, c: 2 (first block 40 > 3), d: 1
+    assert [[sg.blocks[0] for sg in lay.segments] for lay in out] == [[10, 3, 40, 90], [10, 3, 7, 91], [10, 40, 93], [94]]
+    for before, after in zip(lays, out):
+        key = lambda sg: (sg.blocks[0], sg.pos0, sg.length, sg.ctx)
+        assert sorted(map(key, before.segments)) == sorted(map(key, after.segments))
+        assert not after.segments[-1].ctx or all(sg.ctx for sg in after.segments)
+        assert after.length == before.length
