@@ -86,7 +86,8 @@ def test_order_for_reuse_lists_shared_documents_first_and_keeps_everything():
     ]
     out = order_for_reuse(lays)
     # a: 3 requests, b: 2, c: 2 (first block 40 > 3), d: 1
-    assert [[sg.blocks[0] for sg in lay.segments] for lay in out] == [[10, 3, 40, 90], [10, 3, 7, 91], [10, 40, 93], [94]]
+    firsts = [[sg.blocks[0] for sg in lay.segments] for lay in out]
+    assert firsts == [[10, 3, 40, 90], [10, 3, 7, 91], [10, 40, 93], [94]]
     for before, after in zip(lays, out):
         key = lambda sg: (sg.blocks[0], sg.pos0, sg.length, sg.ctx)
         assert sorted(map(key, before.segments)) == sorted(map(key, after.segments))
