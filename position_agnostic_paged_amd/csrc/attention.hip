@@ -90,8 +90,11 @@ __global__ __launch_bounds__(64 * WR) void prefill_kernel(AttnArgs a) {
 // together: with the host listing each request's documents most shared
 // first, a shared document is read for all its requests at about the same
 // time and mostly comes from L2 after the first read.
-template <typename T, int DH, int KIND, bool DEFER, int RB, int WT>
-__global__ __launch_bounds__(64 * WT) void decode_kernel(AttnArgs a) {
+// WPE > 1 asks the compiler for at least WPE resident waves per SIMD (a
+// register cap): the launch picks it for uneven batches, whose many short
+// splits gain from more waves in flight.
+template <typename T, int DH, int KIND, bool DEFER, int RB, int WT, int WPE>
+__global__ __launch_bounds__(64 * WT) __attribute__((amdgpu_waves_per_eu(WPE))) void decode_kernel(AttnArgs a) {
   using W = WaveAttn<T, DH, KIND, DEFER, false, RB>;
   const int lane = threadIdx.x & 63;
 #if LAZY_UNIFORM_WAVE
@@ -253,6 +256,7 @@ int decode_rb(int group) { return group <= 16 ? 1 : group <= 32 ? 2 : group <= 6
 
 struct Plan {
   int rb, wr, wt;
+  bool uneven;  // decode: request lengths far apart (more, shorter splits)
   int row_tiles;
   int splits;  // grid extent along splits
   int chunk;   // tiles per split
@@ -277,6 +281,7 @@ void size_splits(Plan& p, long per_tile_units, int num_reqs, int max_tiles, int6
 
 Plan make_plan(const lazy_geom* g, int num_reqs, int max_q_len, int max_tiles, int64_t total_tiles, bool prefill) {
   Plan p;
+  p.uneven = false;
   const int group = g->num_q_heads / g->num_kv_heads;
   if (prefill) {
     // 4 row blocks per wave when a request has >= 256 query rows (halves the
@@ -293,9 +298,9 @@ Plan make_plan(const lazy_geom* g, int num_reqs, int max_q_len, int max_tiles, i
     p.wr = 1;
     p.wt = kDecodeWT;
     p.row_tiles = 1;
-    const bool uneven = total_tiles > 0 && (double)max_tiles * num_reqs > 1.25 * (double)total_tiles;
+    p.uneven = total_tiles > 0 && (double)max_tiles * num_reqs > 1.25 * (double)total_tiles;
     size_splits(p, g->num_kv_heads, num_reqs, max_tiles, total_tiles,
-                uneven ? LAZY_DECODE_WAVE_TARGET_UNEVEN : LAZY_DECODE_WAVE_TARGET, 32);
+                p.uneven ? LAZY_DECODE_WAVE_TARGET_UNEVEN : LAZY_DECODE_WAVE_TARGET, 32);
     p.rows_bound = num_reqs * g->num_q_heads;
   }
   return p;
@@ -310,7 +315,16 @@ size_t ws_bytes_for(const lazy_geom* g, const Plan& p) {
 template <typename T, int DH, int KIND, bool DEFER, int RB>
 hipError_t launch_decode(const AttnArgs& a, const Plan& p, int num_reqs, int hkv, hipStream_t st) {
   dim3 grid((unsigned)hkv, (unsigned)num_reqs, (unsigned)((p.splits + kDecodeWT - 1) / kDecodeWT));
-  hipLaunchKernelGGL((decode_kernel<T, DH, KIND, DEFER, RB, kDecodeWT>), grid, dim3(64 * kDecodeWT), 0, st, a);
+  // bf16 with one row block fits three waves per SIMD without spilling (168
+  // VGPRs, 200 uncapped); uneven batches run that build, near-uniform ones,
+  // which one resident round of two waves per SIMD serves best, the other
+  if constexpr (std::is_same<T, bf16>::value && RB == 1) {
+    if (p.uneven) {
+      hipLaunchKernelGGL((decode_kernel<T, DH, KIND, DEFER, RB, kDecodeWT, 3>), grid, dim3(64 * kDecodeWT), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_kernel<T, DH, KIND, DEFER, RB, kDecodeWT, 1>), grid, dim3(64 * kDecodeWT), 0, st, a);
   return hipGetLastError();
 }
 

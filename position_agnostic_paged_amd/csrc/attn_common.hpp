@@ -21,14 +21,16 @@
 // Decode split heuristic: about this many waves (one per split and (request,
 // KV head)) per launch.  Requests of near-uniform length: one resident round
 // on 256 CUs at two waves per SIMD (more splits only add partials and tail).
-// Uneven lengths: four rounds, so the dispatcher can balance waves that
+// Uneven lengths: four rounds at three waves per SIMD (the launch picks the
+// three-wave build for them), so the dispatcher can balance waves that
 // progress at different speeds (measured on MI355X: 64 x 32K uniform batch
-// best at 2048, 48 x 8K-66K batch best at 8192).
+// best at 2048; 48 x 8K-66K batch with shared documents 812 us at 12288
+// waves and three per SIMD, 852 us at 8192 and two, 886 us at 12288 and two).
 #ifndef LAZY_DECODE_WAVE_TARGET
 #define LAZY_DECODE_WAVE_TARGET 2048
 #endif
 #ifndef LAZY_DECODE_WAVE_TARGET_UNEVEN
-#define LAZY_DECODE_WAVE_TARGET_UNEVEN 8192
+#define LAZY_DECODE_WAVE_TARGET_UNEVEN 12288
 #endif
 // Prefill split heuristic: about this many workgroups per launch.
 #ifndef LAZY_PREFILL_WG_TARGET
