@@ -250,7 +250,9 @@ __global__ void debug_unpack_kernel(const uint64_t* w, int64_t n, int32_t* blk, 
 namespace {
 
 constexpr int kPrefillWR = 4;  // waves per prefill workgroup (each RB x 16 query rows)
-constexpr int kDecodeWT = 4;                   // 4 waves = 4 splits per workgroup
+// one wave (one split) per workgroup: on the uneven mixed batch 791 us vs 798
+// (two) / 812 (four) / 862 (eight); near-uniform no-sharing batch unchanged
+constexpr int kDecodeWT = 1;
 
 int decode_rb(int group) { return group <= 16 ? 1 : group <= 32 ? 2 : group <= 64 ? 4 : 8; }
 
