@@ -238,3 +238,14 @@ def test_dh64_interleaved_prefill_decode_and_control():
     _check_prefill("small_dh64_interleaved")
     _check_prefill("small_dh64_interleaved", shared=False, prerotated=True)
     _check_decode("small_dh64_interleaved", steps=[0, 1, 2, 3])
+
+
+def test_uneven_decode_prerotated_control_and_alibi():
+    """Uneven batches (7 to 11K tokens) run the decode build limited to three waves per SIMD: its
+    pre-rotated variant (no-sharing control) and its ALiBi variant (group 4), against the oracle."""
+    from workloads.gen import PosSpec
+
+    _check_decode("ragged", steps=[0, 2], shared=False, prerotated=True)
+    wl = make_workload("ragged")
+    wl.pos = PosSpec("alibi")
+    _check_decode_wl(wl, steps=[0, 1], reqs=range(len(wl.decode_reqs)))
