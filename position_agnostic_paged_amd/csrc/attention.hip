@@ -80,8 +80,11 @@ __global__ __launch_bounds__(64 * WR) void prefill_kernel(AttnArgs a) {
 }
 
 // Decode: one wave = the G query heads of one (request, KV head) x one split;
-// a workgroup = WT waves on WT consecutive splits.  Software-pipelined: the
-// next pair's K/V loads are in flight while the current pair is consumed.
+// a workgroup = WT waves on WT consecutive splits.  Each tile pair's K/V is
+// loaded, then consumed, with the next pair's tile words fetched one pair
+// ahead; LAZY_DECODE_PIPELINE builds the variant that keeps the next pair's
+// K/V loads in flight during the products instead (more registers per wave,
+// so fewer waves: slower on this part).
 // Grid (KV head, request, split group), fastest first.  Dispatch deals
 // consecutive workgroups round-robin over the 8 XCDs, so with 8 KV heads
 // every XCD (its own L2) serves one head, and all requests that read a shared
