@@ -249,3 +249,16 @@ def test_uneven_decode_prerotated_control_and_alibi():
     wl = make_workload("ragged")
     wl.pos = PosSpec("alibi")
     _check_decode_wl(wl, steps=[0, 1], reqs=range(len(wl.decode_reqs)))
+
+
+def test_documents_in_request_order_without_reuse_ordering():
+    """The engine lists documents most shared first by default; the request's own order (ordering
+    off) is an equally valid tile list and must give the same attention (prefill and decode)."""
+    from position_agnostic_paged_amd.engine import Engine
+
+    Engine.order_for_reuse = False
+    try:
+        _check_prefill("ragged")
+        _check_decode("ragged", steps=[0, 3])
+    finally:
+        Engine.order_for_reuse = True
