@@ -8,6 +8,7 @@ special cases of the YaRN and ALiBi definitions.
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -154,3 +155,30 @@ def test_alibi_slopes():
     assert s71[-1] == 1.0 / 256
     assert abs(s71[0] - 2 ** (-8 / 71)) < 1e-16
     assert np.all(np.diff(s71) < 0)
+
+
+def _yarn_golden():
+    path = os.path.join(os.path.dirname(__file__), "golden", "yarn_ramp.txt")
+    rows = []
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, th, thp = line.split()
+            rows.append((int(k), float(th), float(thp)))
+    return rows
+
+
+def test_yarn_mid_ramp_hand_derived():
+    """theta'_k inside the ramp equals values derived by hand from the YaRN paper's linear gamma(r)
+    (tests/golden/yarn_ramp.txt): catches a ramp over channel index, a wrong denominator or a
+    non-linear blend, none of which the end-region checks see."""
+    dh, base, s, L = 128, 5e5, 8.0, 8192
+    theta = rope.rope_inv_freq(dh, base)
+    y = rope.yarn_inv_freq(dh, base, s, L)
+    rows = _yarn_golden()
+    assert len(rows) >= 3
+    for k, th, thp in rows:
+        assert abs(theta[k] - th) <= 1e-13 * th, (k, theta[k], th)
+        assert abs(y[k] - thp) <= 1e-13 * thp, (k, y[k], thp)
+    # the two regions the file's derivation names
+    assert y[16] == theta[16] and abs(y[35] - theta[35] / 8) <= 1e-18
