@@ -120,6 +120,11 @@ typedef struct {
 lazy_status lazy_rope_freqs(int32_t head_dim, double base, double yarn_factor, int32_t yarn_orig_ctx,
                             double beta_fast, double beta_slow, double* inv_freq_out, double* logit_gain);
 
+/* Softmax logit multiplier ([N] "Generality": scaled RoPE is metadata): 1/sqrt(head_dim), times the
+ * YaRN temperature gain (0.1 ln s + 1)^2 when yarn_factor s > 1 (ALiBi and plain RoPE pass s <= 1).
+ * The value callers put in lazy_pos_desc.softmax_scale.  Host; pure. */
+lazy_status lazy_softmax_scale(int32_t head_dim, double yarn_factor, float* scale_out);
+
 /* cos/sin table [max_pos][dh] (layout above) from fp64 angles p*theta_k rounded
  * once to fp32 ([N] "Key designs": coefficients from a table, one D-long row
  * per document).  Host memory (caller copies it to the device); pure. */
@@ -157,12 +162,15 @@ lazy_status lazy_unpack_tiles(const uint64_t* words, int64_t n, int64_t* block_i
  * Outputs (host, caller-allocated): tiles_out[tiles_cap] words,
  * tile_start[num_reqs+1] (tile range of request r), ctx_tiles[num_reqs]
  * (number of leading context tiles of r).  Block ids must be < num_blocks.
- * A segment of length 0 emits no tile.  Returns LAZY_ERR_ARG if tiles_cap is
- * too small or any field is out of range.  Pure. */
+ * max_pos > 0 (the rows of the cos/sin table the attention calls will use)
+ * requires every rotary context tile's offset Delta to be < max_pos, since
+ * the kernels read row Delta; pass 0 with the in-kernel sincos path or for
+ * ALiBi.  A segment of length 0 emits no tile.  Returns LAZY_ERR_ARG if
+ * tiles_cap is too small or any field is out of range.  Pure. */
 lazy_status lazy_build_tiles(int32_t kind, int32_t num_reqs, const int32_t* seg_start, const int32_t* seg_len,
                              const int64_t* seg_pos0, const uint8_t* seg_is_ctx, const int32_t* seg_block_start,
-                             const int32_t* blocks, int64_t num_blocks, uint64_t* tiles_out, int64_t tiles_cap,
-                             int32_t* tile_start, int32_t* ctx_tiles);
+                             const int32_t* blocks, int64_t num_blocks, int32_t max_pos, uint64_t* tiles_out,
+                             int64_t tiles_cap, int32_t* tile_start, int32_t* ctx_tiles);
 
 /* ------------------------------------------------------------- device calls */
 
@@ -177,10 +185,14 @@ lazy_status lazy_build_tiles(int32_t kind, int32_t num_reqs, const int32_t* seg_
  * block s / 16, slot s % 16.  Device arrays: k, v [T][Hkv][dh]; q_inout
  * [T][Hq][dh] (nullable, updated in place); positions int32 [T];
  * slot_mapping int64 [T].  A token whose slot is negative is not written to
- * the cache (its q is still rotated).  Device-side guards: a slot >=
- * num_blocks*16, a negative RoPE position, or (with a cos/sin table) a
- * position >= max_pos skips that token (no cache write, q untouched) --
- * callers must pass valid values.
+ * the cache (its q is still rotated).  Positions and slots are device data
+ * the host cannot see, so callers must validate them before the call
+ * (position in [0, max_pos) with a table, [0, 2^24) without; slot <
+ * num_blocks*16).  The kernel never reads or writes outside its buffers: a
+ * slot >= num_blocks*16 is not written, and a RoPE position that is
+ * negative or outside the table turns that token's cache row (and its q
+ * row) into NaN, so an invalid position can only show up as NaN outputs,
+ * never as silently unrotated keys.
  * Rotation math is fp32; stored values are rounded once to T. */
 lazy_status lazy_kv_write(const lazy_geom* geom, const lazy_pos_desc* pos, void* k_cache, void* v_cache,
                           int64_t num_blocks, const void* k, const void* v, void* q_inout,

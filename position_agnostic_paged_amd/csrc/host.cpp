@@ -103,6 +103,16 @@ extern "C" lazy_status lazy_rope_freqs(int32_t head_dim, double base, double yar
   return LAZY_OK;
 }
 
+extern "C" lazy_status lazy_softmax_scale(int32_t head_dim, double yarn_factor, float* scale_out) {
+  clear_error();
+  if (head_dim < 1) return fail(LAZY_ERR_ARG, "head_dim must be >= 1");
+  if (!scale_out) return fail(LAZY_ERR_ARG, "scale_out is NULL");
+  // 1/sqrt(dh) on the logits; YaRN adds its temperature gain (0.1 ln s + 1)^2
+  const double t = yarn_factor > 1.0 ? 0.1 * log(yarn_factor) + 1.0 : 1.0;
+  *scale_out = (float)(t * t / sqrt((double)head_dim));
+  return LAZY_OK;
+}
+
 extern "C" lazy_status lazy_rope_table(int32_t head_dim, const double* inv_freq, int32_t max_pos, float* table_out) {
   clear_error();
   if (head_dim < 2 || head_dim % 2) return fail(LAZY_ERR_ARG, "head_dim must be even and >= 2");
@@ -161,8 +171,8 @@ extern "C" lazy_status lazy_unpack_tiles(const uint64_t* words, int64_t n, int64
 extern "C" lazy_status lazy_build_tiles(int32_t kind, int32_t num_reqs, const int32_t* seg_start,
                                         const int32_t* seg_len, const int64_t* seg_pos0, const uint8_t* seg_is_ctx,
                                         const int32_t* seg_block_start, const int32_t* blocks, int64_t num_blocks,
-                                        uint64_t* tiles_out, int64_t tiles_cap, int32_t* tile_start,
-                                        int32_t* ctx_tiles) {
+                                        int32_t max_pos, uint64_t* tiles_out, int64_t tiles_cap,
+                                        int32_t* tile_start, int32_t* ctx_tiles) {
   clear_error();
   if (kind != LAZY_ROPE_HALF && kind != LAZY_ROPE_INTERLEAVED && kind != LAZY_ALIBI)
     return fail(LAZY_ERR_ARG, "unknown positional kind %d", kind);
@@ -203,6 +213,10 @@ extern "C" lazy_status lazy_build_tiles(int32_t kind, int32_t num_reqs, const in
         if (blk < 0 || blk >= num_blocks)
           return fail(LAZY_ERR_ARG, "segment %d block %d: id %lld outside the pool", s, b, (long long)blk);
         if (off > LAZY_MAX_OFFSET) return fail(LAZY_ERR_ARG, "segment %d: offset %lld exceeds 2^24-1", s, (long long)off);
+        // the kernels read cos/sin row Delta of every rotary context tile
+        if (max_pos > 0 && ctx && kind != LAZY_ALIBI && off >= max_pos)
+          return fail(LAZY_ERR_ARG, "segment %d: document offset %lld outside the cos/sin table (max_pos %d)", s,
+                      (long long)off, max_pos);
         if (nt >= tiles_cap) return fail(LAZY_ERR_ARG, "tiles_cap %lld too small", (long long)tiles_cap);
         tiles_out[nt++] = ((uint64_t)blk << 40) | ((uint64_t)off << 16) | (uint64_t)mask;
         if (ctx) ++nctx;

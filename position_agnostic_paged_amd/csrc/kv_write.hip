@@ -104,6 +104,23 @@ __device__ __forceinline__ void rotate_row(const KvArgs& a, const T* src, T* dst
   }
 }
 
+// The channels rotate_row writes for chunk c, set to NaN (a token whose
+// rotation position is invalid: its row must not pass for a rotated one).
+template <typename T, int DH, int KIND>
+__device__ __forceinline__ void poison_row(T* dst, int c) {
+  using F8 = typename Elem<T>::Frag8;
+  F8 nan;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) nan[t] = Elem<T>::from_f(__builtin_nanf(""));
+  if (KIND == kvHalf) {
+    *reinterpret_cast<F8*>(dst + 8 * c) = nan;
+    *reinterpret_cast<F8*>(dst + DH / 2 + 8 * c) = nan;
+  } else {
+    *reinterpret_cast<F8*>(dst + 16 * c) = nan;
+    *reinterpret_cast<F8*>(dst + 16 * c + 8) = nan;
+  }
+}
+
 // blockIdx.y: 0 = K rows, 1 = V rows, 2 = Q rows
 template <typename T, int DH, int KIND>
 __global__ __launch_bounds__(256) void kv_write_kernel(KvArgs a) {
@@ -118,23 +135,31 @@ __global__ __launch_bounds__(256) void kv_write_kernel(KvArgs a) {
   const int t = (int)(idx / ((int64_t)CPR * heads));
 
   const int pos = a.positions[t];
-  if (KIND != kvAlibi && a.cos_sin != nullptr && (pos < 0 || pos >= a.max_pos)) return;  // outside the table
-  if (KIND != kvAlibi && pos < 0) return;
+  // a rotation position the coefficients cannot serve (negative, or past the
+  // table): the token's rows become NaN instead of being skipped, so the
+  // mistake surfaces in every output that reads them
+  const bool bad_pos = KIND != kvAlibi && (pos < 0 || (a.cos_sin != nullptr && pos >= a.max_pos));
 
   if (which == 2) {
     T* row = reinterpret_cast<T*>(a.q) + ((int64_t)t * a.hq + h) * DH;
-    if (KIND != kvAlibi) rotate_row<T, DH, KIND>(a, row, row, pos, c);
+    if (bad_pos)
+      poison_row<T, DH, KIND>(row, c);
+    else if (KIND != kvAlibi)
+      rotate_row<T, DH, KIND>(a, row, row, pos, c);
     return;
   }
   const int64_t slot = a.slots[t];
-  if (slot < 0 || slot >= a.num_slots) return;
+  if (slot < 0 || slot >= a.num_slots) return;  // never write outside the pool
   const int64_t blk = slot / kBlock;
   const int s = (int)(slot % kBlock);
   const int64_t base = (blk * a.hkv + h) * (int64_t)(kBlock * DH);
   if (which == 0) {
     const T* src = reinterpret_cast<const T*>(a.k) + ((int64_t)t * a.hkv + h) * DH;
     T* dst = reinterpret_cast<T*>(a.k_cache) + base + (int64_t)s * DH;
-    rotate_row<T, DH, KIND>(a, src, dst, pos, c);
+    if (bad_pos)
+      poison_row<T, DH, KIND>(dst, c);
+    else
+      rotate_row<T, DH, KIND>(a, src, dst, pos, c);
   } else {
     const T* src = reinterpret_cast<const T*>(a.v) + ((int64_t)t * a.hkv + h) * DH + 16 * c;
     T* dst = reinterpret_cast<T*>(a.v_cache) + base + (int64_t)(16 * c) * kBlock + s;

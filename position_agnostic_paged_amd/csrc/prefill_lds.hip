@@ -37,6 +37,8 @@
 //   * the two waves sharing a SIMD take each iteration's halves in opposite
 //     orders, so one's matrix products overlap the other's vector, scalar
 //     and LDS work between the same two barriers.
+#include <atomic>
+
 #include "attn_common.hpp"
 
 namespace lazy {
@@ -48,24 +50,33 @@ namespace lazy {
 constexpr int kPrefillWaves = LAZY_PREFILL_WAVES;
 constexpr int kLdsBytes = 160 * 1024;    // LDS of one CU, all of it for the ring
 
-// Wait until at most N vector-memory operations of this wave are outstanding.
+// Wait until at most N vector-memory operations of this wave are outstanding
+// and, before a bare s_barrier, all of its LDS and scalar-memory operations
+// (lgkmcnt 0): the wave's LDS writes (rotated K rows, pair headers) must have
+// completed before other waves read them after the barrier.  The direct
+// global->LDS copies count on vmcnt only, so the later pairs' copies stay in
+// flight.
 template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0x0 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until at most n stages of L copies each are outstanding (n <= MAXN).
+// Only this wave's LDS and scalar-memory operations (vmcnt left at its maximum).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14)); }
+
+// Wait until at most n stages of L copies each are outstanding (n <= MAXN),
+// then for lgkmcnt 0 (every caller is followed by a barrier).
 template <int L, int MAXN>
 __device__ __forceinline__ void wait_stages(int n) {
   if constexpr (MAXN > 0) {
     if (n >= MAXN) {
-      wait_vmcnt<MAXN * L>();
+      wait_vmcnt_lgkm0<MAXN * L>();
       return;
     }
     wait_stages<L, MAXN - 1>(n);
   } else {
-    wait_vmcnt<0>();
+    wait_vmcnt_lgkm0<0>();
   }
 }
 
@@ -509,6 +520,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
     dr[0] = uniform((int)d[0]);
     dr[1] = uniform((int)d[1]);
   }
+  wait_lgkm0();  // the rotated rows of pairs 0 and 1 are written before the barrier publishes them
   asm volatile("s_barrier" ::: "memory");
   f32x4 s[2][RB];
   pl.scores(pl.stage(0), koff, qr, s);
@@ -693,12 +705,19 @@ hipError_t launch_rb(const AttnArgs& a, int row_tiles, int splits, int num_reqs,
   constexpr bool rot = (KIND != kAlibi) && DEFER;
   using SG = StageGeom<DH, rot, NW>;
   const size_t lds = (size_t)SG::kStages * SG::kBytes;
-  static bool attr_set = false;  // the ring needs more than the default 64 KiB of dynamic LDS
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_lds_kernel<DH, KIND, DEFER, RB, NW>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // The ring needs more than the default 64 KiB of dynamic LDS: the attribute
+  // is set once per device (a second setting is harmless, so racing threads
+  // need no lock).
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
+  if (bit == 0 || !(attr_set.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_lds_kernel<DH, KIND, DEFER, RB, NW>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set.fetch_or(bit, std::memory_order_release);
   }
   const int num_wgs = row_tiles * splits * hkv * num_reqs;  // 1-D: the kernel maps ids to units
   hipLaunchKernelGGL((prefill_lds_kernel<DH, KIND, DEFER, RB, NW>), dim3((unsigned)num_wgs), dim3(64 * NW), lds, st, a,

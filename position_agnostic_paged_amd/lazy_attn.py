@@ -30,7 +30,8 @@ BLOCK_SIZE = 16
 KIND_BY_NAME = {"rope_half": LAZY_ROPE_HALF, "rope_interleaved": LAZY_ROPE_INTERLEAVED, "alibi": LAZY_ALIBI}
 
 EXPORTED = [
-    "lazy_rope_freqs", "lazy_rope_table", "lazy_alibi_slopes", "lazy_pack_tiles", "lazy_unpack_tiles",
+    "lazy_rope_freqs", "lazy_softmax_scale", "lazy_rope_table", "lazy_alibi_slopes", "lazy_pack_tiles",
+    "lazy_unpack_tiles",
     "lazy_build_tiles", "lazy_kv_write", "lazy_attn_workspace_size", "lazy_attn_prefill", "lazy_attn_decode",
     "lazy_debug_unpack", "lazy_last_error",
 ]
@@ -64,11 +65,12 @@ def lib() -> C.CDLL:
         P, I32, I64 = C.c_void_p, C.c_int32, C.c_int64
         sig = {
             "lazy_rope_freqs": [I32, C.c_double, C.c_double, I32, C.c_double, C.c_double, P, P],
+            "lazy_softmax_scale": [I32, C.c_double, P],
             "lazy_rope_table": [I32, P, I32, P],
             "lazy_alibi_slopes": [I32, P],
             "lazy_pack_tiles": [P, P, P, I64, P],
             "lazy_unpack_tiles": [P, I64, P, P, P],
-            "lazy_build_tiles": [I32, I32, P, P, P, P, P, P, I64, P, I64, P, P],
+            "lazy_build_tiles": [I32, I32, P, P, P, P, P, P, I64, I32, P, I64, P, P],
             "lazy_kv_write": [P, P, P, P, I64, P, P, P, P, P, I32, P],
             "lazy_attn_prefill": [P, P, P, P, I64, P, P, P, P, P, P, I32, I32, I32, I64, P, P, C.c_size_t, P],
             "lazy_attn_decode": [P, P, P, P, I64, P, P, P, P, P, I32, I32, I64, P, P, C.c_size_t, P],
@@ -126,6 +128,12 @@ def rope_freqs(head_dim: int, base: float, yarn_factor: float = 1.0, yarn_orig_c
     return out, gain.value
 
 
+def softmax_scale(head_dim: int, yarn_factor: float = 1.0) -> float:
+    out = C.c_float(0.0)
+    _check(lib().lazy_softmax_scale(head_dim, yarn_factor, C.cast(C.pointer(out), C.c_void_p)))
+    return out.value
+
+
 def rope_table(head_dim: int, inv_freq: np.ndarray, max_pos: int) -> np.ndarray:
     inv = np.ascontiguousarray(inv_freq, np.float64)
     out = np.empty((max_pos, head_dim), np.float32)
@@ -158,8 +166,9 @@ def unpack_tiles(words):
 
 
 def build_tiles(kind: int, seg_start, seg_len, seg_pos0, seg_is_ctx, seg_block_start, blocks, num_blocks: int,
-                tiles_cap: Optional[int] = None):
-    """Tile words, tile_start [R+1], ctx_tiles [R] of every request (host arrays)."""
+                tiles_cap: Optional[int] = None, max_pos: int = 0):
+    """Tile words, tile_start [R+1], ctx_tiles [R] of every request (host arrays); max_pos > 0 checks every
+    rotary document offset against the cos/sin table's rows."""
     ss = np.ascontiguousarray(seg_start, np.int32)
     sl = np.ascontiguousarray(seg_len, np.int32)
     sp = np.ascontiguousarray(seg_pos0, np.int64)
@@ -172,7 +181,8 @@ def build_tiles(kind: int, seg_start, seg_len, seg_pos0, seg_is_ctx, seg_block_s
     tstart = np.empty(R + 1, np.int32)
     nctx = np.empty(max(R, 1), np.int32)
     _check(lib().lazy_build_tiles(kind, R, _np_ptr(ss), _np_ptr(sl), _np_ptr(sp), _np_ptr(sc), _np_ptr(sb),
-                                  _np_ptr(bl), num_blocks, _np_ptr(tiles), cap, _np_ptr(tstart), _np_ptr(nctx)))
+                                  _np_ptr(bl), num_blocks, max_pos, _np_ptr(tiles), cap, _np_ptr(tstart),
+                                  _np_ptr(nctx)))
     return tiles[: tstart[R]].copy(), tstart, nctx[:R].copy()
 
 

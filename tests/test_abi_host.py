@@ -79,7 +79,7 @@ def _golden_request():
     return segs, rows[1:]
 
 
-def _build(L, kind, reqs, num_blocks=1 << 20):
+def _build(L, kind, reqs, num_blocks=1 << 20, max_pos=0):
     seg_start, seg_len, seg_pos0, seg_ctx, seg_bs, blocks = [0], [], [], [], [0], []
     for segs in reqs:
         for s in segs:
@@ -90,7 +90,7 @@ def _build(L, kind, reqs, num_blocks=1 << 20):
             seg_bs.append(len(blocks))
         seg_start.append(len(seg_len))
     return L.build_tiles(kind, seg_start, seg_len, seg_pos0, seg_ctx, seg_bs, blocks or [0], num_blocks,
-                         max(1, len(blocks)))
+                         max(1, len(blocks)), max_pos)
 
 
 def test_build_tiles_golden(L):
@@ -138,6 +138,52 @@ def test_build_tiles_rejects_bad_layouts(L):
         _build(L, 0, [[{"blocks": [0], "len": 17, "pos0": 0, "ctx": True}]])
     with pytest.raises(L.LazyError):  # offset beyond 24 bits
         _build(L, 2, [[{"blocks": [0], "len": 5, "pos0": 1 << 24, "ctx": True}]])
+
+
+def test_build_tiles_checks_offsets_against_the_table(L):
+    """A rotary document offset must address a row of the cos/sin table the kernels read; private tiles
+    and ALiBi offsets are never table rows."""
+    doc = {"blocks": [0, 1], "len": 20, "pos0": 100, "ctx": True}
+    priv = {"blocks": [2], "len": 3, "pos0": 120, "ctx": False}
+    _build(L, 0, [[doc, priv]], max_pos=101)  # Delta = 100 < 101
+    with pytest.raises(L.LazyError, match="cos/sin table"):
+        _build(L, 0, [[doc, priv]], max_pos=100)
+    with pytest.raises(L.LazyError, match="cos/sin table"):
+        _build(L, 1, [[doc, priv]], max_pos=50)
+    _build(L, 2, [[doc, priv]], max_pos=50)  # ALiBi: no table row is read
+    _build(L, 0, [[{"blocks": [0], "len": 3, "pos0": 500, "ctx": False}]], max_pos=10)  # private tile
+    _build(L, 0, [[doc, priv]], max_pos=0)  # 0: no table (in-kernel sincos)
+
+
+def test_softmax_scale_matches_oracle(L):
+    """The logit multiplier the library hands the kernels: 1/sqrt(dh), times the YaRN gain."""
+    from workloads.gen import PosSpec
+
+    for dh, s in ((64, 1.0), (128, 1.0), (128, 8.0), (128, 4.0)):
+        spec = PosSpec("rope_half", base=5e5, yarn_factor=s, yarn_orig_ctx=8192 if s > 1 else 0)
+        want = OR.variant(spec, dh, 8)["scale"]
+        assert L.softmax_scale(dh, s) == pytest.approx(want, rel=1e-7)
+    assert L.softmax_scale(64, 1.0) == np.float32(0.125)
+
+
+def test_engine_validates_kv_write_positions_and_slots():
+    """Positions outside the cos/sin table and slots outside the pool are refused on the host, before any
+    launch (the library sees them only on the device)."""
+    from position_agnostic_paged_amd.engine import Engine, PosDesc
+
+    pos = PosDesc("rope_half", 64, 4, "cpu", base=1e4, max_pos=100)
+    eng = Engine(4, 1, 64, "fp32", pos, 8, "cpu")
+    eng.check_write(np.array([0, 99]), np.array([0, 127]))
+    with pytest.raises(ValueError, match="rotation positions"):
+        eng.check_write(np.array([0, 100]), np.array([0, 1]))
+    with pytest.raises(ValueError, match="rotation positions"):
+        eng.check_write(np.array([-1]), np.array([0]))
+    with pytest.raises(ValueError, match="outside the pool"):
+        eng.check_write(np.array([0]), np.array([128]))
+    alibi = Engine(4, 1, 64, "fp32", PosDesc("alibi", 64, 4, "cpu"), 8, "cpu")
+    alibi.check_write(np.array([10_000]), np.array([5]))  # ALiBi keys are not rotated
+    fly = Engine(4, 1, 64, "fp32", PosDesc("rope_half", 64, 4, "cpu", base=1e4, on_the_fly=True), 8, "cpu")
+    fly.check_write(np.array([(1 << 24) - 1]), np.array([0]))
 
 
 @pytest.mark.parametrize("dh,base,s", [(64, 1e4, 1.0), (128, 5e5, 1.0), (128, 5e5, 8.0)])

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests.harness import TOL, max_abs, oracle_decode, oracle_prefill, say
+from tests.harness import Gate, nodelta_decode, nodelta_prefill, oracle_decode, oracle_prefill, say
 from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
@@ -37,8 +37,11 @@ def _prefill(wl, poison):
     out = sc.run().float().cpu().numpy()
     torch.cuda.synchronize()
     want = oracle_prefill(wl, 0, range(len(sc.reqs)))
-    err = max(max_abs(out[sc.q_start_h[i]: sc.q_start_h[i + 1]], w) for i, w in enumerate(want))
-    return out, err
+    gate = Gate(f"{wl.name} prefill poison={poison}", wl.geom.dtype)
+    for i, w in enumerate(want):
+        gate.add(out[sc.q_start_h[i]: sc.q_start_h[i + 1]], w)
+        gate.add_negative(nodelta_prefill(wl, 0, i), w)
+    return out, gate
 
 
 def _decode(wl, poison, steps):
@@ -52,11 +55,13 @@ def _decode(wl, poison, steps):
         if s in steps:
             got[s] = out.float().cpu().numpy()
     torch.cuda.synchronize()
-    err = 0.0
+    gate = Gate(f"{wl.name} decode poison={poison}", wl.geom.dtype)
     for r in range(len(wl.decode_reqs)):
-        for s, w in zip(steps, oracle_decode(wl, r, steps, draws)):
-            err = max(err, max_abs(got[s][r], w))
-    return got, err
+        want = oracle_decode(wl, r, steps, draws)
+        for s, w in zip(steps, want):
+            gate.add(got[s][r], w)
+        gate.add_negative(nodelta_decode(wl, r, steps[0]), want[0])
+    return got, gate
 
 
 @pytest.mark.parametrize("key", ["ragged", "tiny_fp32", "small_dh64_interleaved", "falcon7b_alibi_prefill"])
@@ -64,19 +69,19 @@ def test_nan_poisoned_unused_slots_prefill(key):
     """Documents of 1..999 tokens (partial last blocks) in a pool filled with NaN before any write:
     the staged bf16 kernel (RoPE half-split, interleaved, ALiBi) and the fp32 per-wave kernel."""
     wl = make_workload(key)
-    out, err = _prefill(wl, poison=True)
-    say(f"[nan-poisoned prefill] {wl.name}: max-abs err {err:.3e} (tol {TOL[wl.geom.dtype]})")
+    say(f"[nan-poisoned prefill] {wl.name}")
+    out, gate = _prefill(wl, poison=True)
     assert np.isfinite(out).all()
-    assert err <= TOL[wl.geom.dtype]
+    gate.check()
 
 
 @pytest.mark.parametrize("key", ["ragged", "tiny_fp32"])
 def test_nan_poisoned_unused_slots_decode(key):
     wl = make_workload(key)
-    got, err = _decode(wl, poison=True, steps=[0, 2])
-    say(f"[nan-poisoned decode] {wl.name}: max-abs err {err:.3e} (tol {TOL[wl.geom.dtype]})")
+    say(f"[nan-poisoned decode] {wl.name}")
+    got, gate = _decode(wl, poison=True, steps=[0, 2])
     assert all(np.isfinite(g).all() for g in got.values())
-    assert err <= TOL[wl.geom.dtype]
+    gate.check()
 
 
 def test_same_document_at_two_offsets_in_one_request():
@@ -97,9 +102,8 @@ def test_same_document_at_two_offsets_in_one_request():
             DecodeRequest(doc_ids=[c, c], k=wl.decode_reqs[0].k, v=wl.decode_reqs[0].v)]
     wl.decode_reqs = decs
     say(f"[repeated documents] prefill {[r.doc_ids for r in pre]}, decode {[r.doc_ids for r in decs]}")
-    out, err_p = _prefill(wl, poison=False)
-    say(f"  prefill max-abs err {err_p:.3e}")
-    got, err_d = _decode(wl, poison=False, steps=[0, 1])
-    say(f"  decode max-abs err {err_d:.3e}")
+    out, gate_p = _prefill(wl, poison=False)
+    got, gate_d = _decode(wl, poison=False, steps=[0, 1])
     assert np.isfinite(out).all()
-    assert err_p <= TOL[wl.geom.dtype] and err_d <= TOL[wl.geom.dtype]
+    gate_p.check()
+    gate_d.check()

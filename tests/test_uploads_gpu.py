@@ -34,10 +34,11 @@ def test_step_uploads_round_trip_and_tile_table():
 
 
 def test_step_uploads_overlap_never_overwrites_a_buffer_in_use():
-    """Commits back to back with no host synchronisation while the compute
-    stream lags behind (a spinning kernel before each read): every step's
-    device views must still hold that step's data when its kernels run, even
-    though the copies of later steps run on their own stream."""
+    """Commits back to back with no host synchronisation while the device
+    lags behind (a spinning kernel before each read): every step's device
+    views must still hold that step's data when its kernels run.  The copies
+    are enqueued on the current stream, behind the earlier steps' kernels, and
+    a pinned buffer is refilled only after its previous copy has executed."""
     from position_agnostic_paged_amd.engine import StepUploads
 
     rng = np.random.default_rng(5)

@@ -17,4 +17,7 @@ from .gen import (  # noqa: F401
     Workload,
     make_workload,
     round_to_bf16,
+    sharpened,
+    zipf_accesses,
+    zipf_trace,
 )

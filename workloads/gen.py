@@ -12,6 +12,8 @@ of draw:
     5  queries of a document's own tokens (the document-processing pass
        that writes its cache entry on a miss; per document id), and extra
        question draws keyed by a caller-chosen id
+    6  independent (document, position) accesses of a static-cache
+       hit-ratio trace
 
 so any single document, request or step can be regenerated on its own.  Draws
 are fp32 normals; bf16 workloads round them to the nearest bf16 (ties to even)
@@ -90,6 +92,7 @@ class Workload:
     num_decode_steps: int = 0
     description: str = ""
     kv_budget_blocks: Optional[int] = None  # document-cache budget in blocks (None = unlimited)
+    q_scale: float = 1.0  # multiplier on decode-step queries (a power of two: exact in bf16)
     _doc_cache: Dict[int, Tuple[np.ndarray, np.ndarray]] = field(default_factory=dict, repr=False)
 
     # ----------------------------------------------------------------- draws
@@ -136,6 +139,8 @@ class Workload:
         kv *= np.float32(self.kv_scale)
         if g.dtype == "bf16":
             q, kv = round_to_bf16(q), round_to_bf16(kv)
+        if self.q_scale != 1.0:
+            q = q * np.float32(self.q_scale)  # exact: a power of two
         return q, kv[0], kv[1]
 
     # ------------------------------------------------------------ structure
@@ -160,6 +165,23 @@ def _zipf_pick(wid: int, req_key: List[int], pool: int, n: int, alpha: float) ->
     w = np.arange(1, pool + 1, dtype=np.float64) ** (-alpha)
     ids = rng.choice(pool, size=n, replace=False, p=w / w.sum())
     return [int(i) for i in rng.permutation(ids)]
+
+
+def zipf_trace(seed: int, num_docs: int, docs_per_req: int, num_reqs: int, alpha: float) -> List[List[int]]:
+    """A retrieval trace: each request draws docs_per_req distinct documents from a pool of num_docs with
+    Zipf(alpha) popularity by id rank (rank 1 = document 0) and places them in a random order; requests
+    are independent.  Seeded by (seed, request index), stream 1 as for the workloads' requests."""
+    return [_zipf_pick(seed, [r], num_docs, docs_per_req, alpha) for r in range(num_reqs)]
+
+
+def zipf_accesses(seed: int, num_docs: int, n: int, alpha: float, positions: int) -> Tuple[np.ndarray, np.ndarray]:
+    """n independent (document, position slot) accesses: documents Zipf(alpha) by id rank, slots uniform
+    over ``positions`` (the static-cache setting of the pages' hit-ratio formula)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 6]))
+    w = np.arange(1, num_docs + 1, dtype=np.float64) ** (-alpha)
+    docs = rng.choice(num_docs, size=n, p=w / w.sum())
+    slots = rng.integers(0, positions, size=n)
+    return docs, slots
 
 
 def _question(wl: Workload, req_key: List[int], Lq: int, with_q: bool):
@@ -231,7 +253,7 @@ def _decode_llama8b() -> Workload:
     return wl
 
 
-def _mixed_llama70b(num_steps: int = 16) -> Workload:
+def _mixed_llama70b(num_steps: int = 16, prefill_alpha: float = 2.1) -> Workload:
     wl = Workload(
         name="llama70b_mixed_yarn8_p4x7.5k_d48x8k-64k",
         wid=4,
@@ -259,7 +281,7 @@ def _mixed_llama70b(num_steps: int = 16) -> Workload:
         reqs = []
         for j in range(4):
             pr = _question(wl, [s, j], 64, True)
-            pr.doc_ids = _zipf_pick(4, [s, j], 1000, 15, 2.1)
+            pr.doc_ids = _zipf_pick(4, [s, j], 1000, 15, prefill_alpha)
             reqs.append(pr)
         steps.append(reqs)
     wl.prefill_steps = steps
@@ -441,3 +463,18 @@ WORKLOADS = {
 
 def make_workload(key: str, **kw) -> Workload:
     return WORKLOADS[key](**kw)
+
+
+def sharpened(wl: Workload, factor: float = 4.0) -> Workload:
+    """The same workload with every query multiplied by ``factor`` (a power of two, so bf16 values stay
+    exact): scores grow by the factor and attention concentrates on fewer keys, so outputs are larger
+    and depend more on where each key sits."""
+    m, e = np.frexp(factor)
+    if factor <= 0 or m != 0.5:
+        raise ValueError("the sharpening factor must be a power of two")
+    wl.q_scale *= factor
+    wl.name = f"{wl.name}_q{factor:g}x"
+    for step in wl.prefill_steps:
+        for r in step:
+            r.q = r.q * np.float32(factor)
+    return wl
