@@ -24,6 +24,8 @@ Modules
   pack       the 64-bit (block id, offset, mask) tile word and the tile list
              a request implies
   zipf       position-agnostic vs position-aware hit-ratio closed form
+  lru        hit/miss sequence of a whole-entry LRU cache under a budget
+             (position-agnostic and position-aware keys alike)
 
 Pins (tests/test_oracle_*.py) tie each function to something other than
 itself; ``rope.yarn_inv_freq`` and ``attention`` are pinned through special
@@ -31,4 +33,4 @@ cases, library routines and brute force (see the tests).  No function here is
 "parity unpinned".
 """
 
-from . import attention, brute, pack, rope, zipf  # noqa: F401
+from . import attention, brute, lru, pack, rope, zipf  # noqa: F401

@@ -11,14 +11,14 @@ the computation runs in liblazyattn.
 
 from __future__ import annotations
 
-import math
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
 
 from . import lazy_attn as L
-from .paging import BlockPool, DocCache, RequestLayout, Segment, blocks_for, flatten_layouts, order_for_reuse
+from .paging import (BlockPool, DocCache, PositionAwareCache, RequestLayout, Segment, blocks_for, flatten_layouts,
+                     order_for_reuse)
 
 TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
 
@@ -33,21 +33,34 @@ class PosDesc:
         self.kind_id = L.KIND_BY_NAME[kind]
         self.head_dim = head_dim
         self.table = self.inv_freq = self.slopes = None
-        gain = 1.0
         if kind == "alibi":
             self.slopes = torch.from_numpy(L.alibi_slopes(num_q_heads)).to(device)
             max_pos = max(max_pos, 1)
         else:
-            inv, gain = L.rope_freqs(head_dim, base, yarn_factor, yarn_orig_ctx, beta_fast, beta_slow)
+            inv, _ = L.rope_freqs(head_dim, base, yarn_factor, yarn_orig_ctx, beta_fast, beta_slow)
             self.inv_freq = torch.from_numpy(inv).to(device)
             if not on_the_fly:
                 if max_pos < 1:
                     raise ValueError("max_pos must cover every rotation position")
                 self.table = torch.from_numpy(L.rope_table(head_dim, inv, max_pos)).to(device)
         self.max_pos = max_pos
-        self.softmax_scale = gain / math.sqrt(head_dim)
+        self.softmax_scale = L.softmax_scale(head_dim, yarn_factor if kind != "alibi" else 1.0)
         self.c = L.PosDescC(self.kind_id, L.LAZY_FLAG_PREROTATED if prerotated else 0, max_pos,
                             self.softmax_scale, L._dev(self.table), L._dev(self.inv_freq), L._dev(self.slopes))
+
+    @property
+    def table_rows(self) -> int:
+        """Rows of the cos/sin table the kernels index by position (0: no table)."""
+        return self.max_pos if self.table is not None else 0
+
+    def check_positions(self, positions: np.ndarray) -> None:
+        """Rotation positions must address the table (or the in-kernel sincos range)."""
+        if self.kind == "alibi" or positions.size == 0:
+            return
+        lo, hi = int(positions.min()), int(positions.max())
+        limit = self.table_rows if self.table is not None else (1 << 24)
+        if lo < 0 or hi >= limit:
+            raise ValueError(f"rotation positions [{lo}, {hi}] outside [0, {limit})")
 
     def with_flags(self, prerotated: bool) -> L.PosDescC:
         c = L.PosDescC.from_buffer_copy(self.c)
@@ -127,11 +140,11 @@ class TileTable:
     its own, or staged into a step's ``StepUploads``)."""
 
     def __init__(self, layouts: Sequence[RequestLayout], kind_id: int, num_blocks: int, device,
-                 uploads: Optional[StepUploads] = None):
+                 uploads: Optional[StepUploads] = None, max_pos: int = 0):
         f = flatten_layouts(layouts)
         cap = sum(blocks_for(n) for n in f["seg_len"]) or 1
         tiles, tstart, nctx = L.build_tiles(kind_id, f["seg_start"], f["seg_len"], f["seg_pos0"], f["seg_is_ctx"],
-                                            f["seg_block_start"], f["blocks"] or [0], num_blocks, cap)
+                                            f["seg_block_start"], f["blocks"] or [0], num_blocks, cap, max_pos)
         self.host_tiles, self.host_start, self.host_ctx = tiles, tstart, nctx
         self.num_reqs = len(layouts)
         self.max_tiles = int(np.max(np.diff(tstart))) if len(layouts) else 0
@@ -150,7 +163,7 @@ class TileTable:
 
 class Engine:
     def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str, pos: PosDesc,
-                 num_blocks: int, device="cuda", budget_blocks: Optional[int] = None):
+                 num_blocks: int, device="cuda", budget_blocks: Optional[int] = None, position_aware: bool = False):
         self.geom = L.make_geom(num_q_heads, num_kv_heads, head_dim, dtype)
         self.hq, self.hkv, self.dh, self.dtype = num_q_heads, num_kv_heads, head_dim, dtype
         self.tdtype = TORCH_DTYPE[dtype]
@@ -160,7 +173,8 @@ class Engine:
         self.k_cache = torch.empty((num_blocks, num_kv_heads, 16, head_dim), dtype=self.tdtype, device=self.device)
         self.v_cache = torch.empty((num_blocks, num_kv_heads, head_dim, 16), dtype=self.tdtype, device=self.device)
         self.pool = BlockPool(num_blocks)
-        self.docs = DocCache(self.pool, budget_blocks)
+        # position_aware: the design the pages compare against, one copy per (document, offset)
+        self.docs = (PositionAwareCache if position_aware else DocCache)(self.pool, budget_blocks)
         self._ws: Optional[torch.Tensor] = None
 
     # ------------------------------------------------------------- writing
@@ -168,6 +182,17 @@ class Engine:
                  slots: torch.Tensor, pos: Optional[L.PosDescC] = None, stream=None) -> None:
         L.kv_write(self.geom, self.pos.c if pos is None else pos, self.k_cache, self.v_cache, self.num_blocks, k, v, q,
                    positions, slots, stream)
+
+    def check_write(self, positions: np.ndarray, slots: np.ndarray) -> None:
+        """Host-side validation of a kv-write's positions and slots (the library sees them only on the
+        device): every position inside the rotation range, every slot inside the pool."""
+        positions = np.asarray(positions)
+        slots = np.asarray(slots)
+        if positions.shape != slots.shape:
+            raise ValueError("positions and slots differ in length")
+        self.pos.check_positions(positions)
+        if slots.size and int(slots.max()) >= self.num_blocks * 16:
+            raise ValueError(f"slot {int(slots.max())} outside the pool of {self.num_blocks} blocks")
 
     def slots_for(self, blocks: Sequence[int], length: int, first: int = 0) -> np.ndarray:
         """Slot ids of tokens first .. first+length-1 of a segment stored in ``blocks``."""
@@ -184,8 +209,11 @@ class Engine:
         n = k.shape[0]
         if n == 0:
             return
-        positions = torch.arange(pos0 + first, pos0 + first + n, dtype=torch.int32).to(self.device)
-        slots = torch.from_numpy(self.slots_for(blocks, n, first)).to(self.device)
+        pos_h = np.arange(pos0 + first, pos0 + first + n, dtype=np.int32)
+        slots_h = self.slots_for(blocks, n, first)
+        self.check_write(pos_h, slots_h)
+        positions = torch.from_numpy(pos_h).to(self.device)
+        slots = torch.from_numpy(slots_h).to(self.device)
         self.kv_write(k, v, q, positions, slots, stream=stream)
 
     def cache_doc(self, doc_id: int, length: int, content_fn, reserve: int = 0) -> Tuple[List[int], bool]:
@@ -194,6 +222,18 @@ class Engine:
         if not hit:
             k, v = content_fn()
             self.write_segment(blocks, k, v, 0)
+        return blocks, hit
+
+    def cache_doc_at(self, doc_id: int, offset: int, length: int, content_fn, reserve: int = 0) -> Tuple[List[int], bool]:
+        """Position-aware cache: pin the copy of a document placed at one global offset, writing it on a miss
+        with RoPE at its global positions offset .. offset+L-1 (the eager re-encode a position-aware cache
+        needs for every new offset).  Attention over such copies runs with LAZY_FLAG_PREROTATED."""
+        if not isinstance(self.docs, PositionAwareCache):
+            raise ValueError("cache_doc_at needs an engine built with position_aware=True")
+        blocks, hit = self.docs.acquire_at(doc_id, offset, length, reserve)
+        if not hit:
+            k, v = content_fn()
+            self.write_segment(blocks, k, v, offset)
         return blocks, hit
 
     def process_documents(self, items: Sequence[Tuple[int, torch.Tensor, torch.Tensor, torch.Tensor]],
@@ -233,6 +273,7 @@ class Engine:
                 layouts.append(RequestLayout([Segment(blocks, n, 0, False)]))
                 pos.append(np.arange(n, dtype=np.int32))
                 slots.append(self.slots_for(blocks, n))
+            self.check_write(np.concatenate(pos), np.concatenate(slots))
             K = torch.cat([it[1] for it in items]).contiguous()
             V = torch.cat([it[2] for it in items]).contiguous()
             Q = torch.cat([it[3] for it in items]).contiguous()
@@ -268,7 +309,7 @@ class Engine:
     def tile_table(self, layouts: Sequence[RequestLayout], uploads: Optional[StepUploads] = None) -> TileTable:
         if self.order_for_reuse:
             layouts = order_for_reuse(layouts)
-        return TileTable(layouts, self.pos.kind_id, self.num_blocks, self.device, uploads)
+        return TileTable(layouts, self.pos.kind_id, self.num_blocks, self.device, uploads, self.pos.table_rows)
 
     def prefill(self, tt: TileTable, q: torch.Tensor, q_start: torch.Tensor, q_pos0: torch.Tensor, max_q_len: int,
                 out: Optional[torch.Tensor] = None, pos: Optional[L.PosDescC] = None, stream=None) -> torch.Tensor:

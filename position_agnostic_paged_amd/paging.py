@@ -7,6 +7,12 @@ the top-C documents instead of floor(C/D) position variants; repository
 landing page, "Demo": one copy per document reused regardless of slot).
 Documents are cached whole and evicted whole in least-recently-used order;
 documents referenced by the work in flight are pinned.
+
+``PositionAwareCache`` is the design the pages compare against (the notes'
+"Background and motivation"; the gist.science summary, "Contesto": existing
+systems materialise a re-encoded copy per position): an entry is a document
+at one global offset, so the same document at another offset is a miss and
+takes another copy from the same budget.
 """
 
 from __future__ import annotations
@@ -110,23 +116,26 @@ class DocCache:
         self.used -= len(d.blocks)
 
     def _make_room(self, need: int) -> None:
-        def room() -> int:
-            return min(self.budget - self.used, self.pool.free_blocks)
-
-        if room() >= need:
+        room = min(self.budget - self.used, self.pool.free_blocks)
+        if room >= need:
             return
-        for doc_id in list(self._docs.keys()):  # least recently used first
-            if room() >= need:
+        # least recently used first, skipping pinned entries; victims are
+        # chosen before any is removed, so the walk stops as soon as enough
+        # room is found (no pass over the whole cache per miss)
+        victims, gain = [], 0
+        for key, d in self._docs.items():
+            if room + gain >= need:
                 break
-            d = self._docs[doc_id]
-            if d.pins > 0:
-                continue
-            del self._docs[doc_id]
+            if d.pins == 0:
+                victims.append(key)
+                gain += len(d.blocks)
+        if room + gain < need:
+            raise CacheFull(f"cannot free {need} blocks: everything left is pinned")
+        for key in victims:
+            d = self._docs.pop(key)
             self.pool.free(d.blocks)
             self.used -= len(d.blocks)
             self.evictions += 1
-        if room() < need:
-            raise CacheFull(f"cannot free {need} blocks: everything left is pinned")
 
     def room_for_private(self, n: int) -> bool:
         """Whether n private blocks fit the budget after evicting every unpinned document."""
@@ -142,6 +151,22 @@ class DocCache:
     def give_back_private(self, blocks: Sequence[int]) -> None:
         self.pool.free(blocks)
         self.used -= len(blocks)
+
+
+class PositionAwareCache(DocCache):
+    """Entries keyed by (document, global offset): a copy is valid at one offset only (its keys carry RoPE at
+    their global positions), so every new offset of a document is a miss and a new copy under the same
+    budget and the same whole-entry LRU eviction."""
+
+    def acquire_at(self, doc_id: int, offset: int, length: int, reserve: int = 0) -> Tuple[List[int], bool]:
+        return self.acquire((doc_id, offset), length, reserve)
+
+    def release_at(self, doc_id: int, offset: int) -> None:
+        self.release((doc_id, offset))
+
+    def copies(self, doc_id: int) -> int:
+        """Cached copies of one document (one per offset it is held at)."""
+        return sum(1 for k in self._docs if k[0] == doc_id)
 
 
 @dataclass

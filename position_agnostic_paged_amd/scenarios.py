@@ -14,6 +14,10 @@ K/V bytes.  ``prerotated=True`` (with shared=False) writes those copies
 already rotated at their global positions and runs the kernels built without
 deferral (LAZY_FLAG_PREROTATED): the "same kernel on pre-rotated K" control of
 the overhead measurement, with an identical tile table and access pattern.
+``aware=True`` (on an engine built with position_aware=True) is the
+position-aware cache the pages compare against: requests that place a
+document at the same offset share its copy, every other offset takes a copy
+of its own, written pre-rotated at that offset.
 """
 
 from __future__ import annotations
@@ -24,7 +28,7 @@ import numpy as np
 import torch
 
 from .engine import Engine, PosDesc, TORCH_DTYPE
-from .paging import RequestLayout, Segment, blocks_for, layout_request
+from .paging import PositionAwareCache, RequestLayout, Segment, blocks_for, layout_request
 
 
 def make_pos(wl, device, max_pos: Optional[int] = None, on_the_fly: bool = False) -> PosDesc:
@@ -46,9 +50,17 @@ def max_position(wl) -> int:
     return m
 
 
-def blocks_needed(wl, shared: bool = True) -> int:
+def blocks_needed(wl, shared: bool = True, aware: bool = False) -> int:
     """Physical blocks for every document and private segment of the workload (no eviction)."""
-    if shared:
+    if aware:
+        placed = set()
+        for step in wl.prefill_steps:
+            for req in step:
+                placed |= _placements(wl, req.doc_ids)
+        for req in wl.decode_reqs:
+            placed |= _placements(wl, req.doc_ids)
+        n = sum(blocks_for(wl.doc_lens[d]) for d, _ in placed)
+    elif shared:
         n = sum(blocks_for(wl.doc_lens[d]) for d in wl.all_doc_ids())
     else:
         n = 0
@@ -65,16 +77,29 @@ def blocks_needed(wl, shared: bool = True) -> int:
     return n
 
 
+def _placements(wl, doc_ids) -> set:
+    """(document, global offset) of each document of a request laid out from position 0."""
+    out, pos = set(), 0
+    for d in doc_ids:
+        out.add((d, pos))
+        pos += wl.doc_lens[d]
+    return out
+
+
 def _to_dev(x: np.ndarray, dtype, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=dtype)
 
 
 class _Base:
-    def __init__(self, wl, engine: Engine, shared: bool, prerotated: bool):
-        if prerotated and shared:
+    def __init__(self, wl, engine: Engine, shared: bool, prerotated: bool, aware: bool = False):
+        if aware:
+            if not isinstance(engine.docs, PositionAwareCache):
+                raise ValueError("the position-aware layout needs an engine built with position_aware=True")
+            shared, prerotated = True, True  # copies shared per (document, offset), written at global positions
+        elif prerotated and shared:
             raise ValueError("pre-rotated copies are private by construction (shared=False)")
         self.wl, self.eng = wl, engine
-        self.shared, self.prerotated = shared, prerotated
+        self.shared, self.prerotated, self.aware = shared, prerotated, aware
         self.tdtype = TORCH_DTYPE[wl.geom.dtype]
         self.dev = engine.device
         self.doc_writes = 0
@@ -97,7 +122,11 @@ class _Base:
         segs, pos = [], 0
         for d in doc_ids:
             L = self.wl.doc_lens[d]
-            if self.shared:
+            if self.aware:
+                blocks, hit = self.eng.cache_doc_at(d, pos, L, lambda d=d: self._doc_dev(d))
+                self.doc_writes += 0 if hit else 1
+                segs.append(Segment(list(blocks), L, pos, True))
+            elif self.shared:
                 blocks, hit = self.eng.cache_doc(d, L, lambda d=d: self._doc_dev(d))
                 self.doc_writes += 0 if hit else 1
                 segs.append(Segment(list(blocks), L, pos, True))
@@ -115,8 +144,9 @@ class _Base:
 class PrefillScenario(_Base):
     """One prefill batch: requests = cached documents + a question whose rows are the queries."""
 
-    def __init__(self, wl, engine: Engine, step: int = 0, shared: bool = True, prerotated: bool = False):
-        super().__init__(wl, engine, shared, prerotated)
+    def __init__(self, wl, engine: Engine, step: int = 0, shared: bool = True, prerotated: bool = False,
+                 aware: bool = False):
+        super().__init__(wl, engine, shared, prerotated, aware)
         reqs = wl.prefill_steps[step]
         self.reqs = reqs
         lq = [r.q.shape[0] for r in reqs]
@@ -160,8 +190,8 @@ class DecodeScenario(_Base):
     """Decode steps of a fixed batch: documents + optional question, then one new token per step."""
 
     def __init__(self, wl, engine: Engine, shared: bool = True, prerotated: bool = False,
-                 prebuild_tables: bool = False, num_steps: Optional[int] = None):
-        super().__init__(wl, engine, shared, prerotated)
+                 prebuild_tables: bool = False, num_steps: Optional[int] = None, aware: bool = False):
+        super().__init__(wl, engine, shared, prerotated, aware)
         self.num_steps = wl.num_decode_steps if num_steps is None else num_steps
         R = len(wl.decode_reqs)
         self.R = R
@@ -208,6 +238,7 @@ class DecodeScenario(_Base):
         q, k, v = self.wl.decode_step(step)
         pos = self.positions(step)
         slots = self.slots(step)
+        self.eng.check_write(pos, slots)
         t = (_to_dev(q, self.tdtype, self.dev), _to_dev(k, self.tdtype, self.dev), _to_dev(v, self.tdtype, self.dev),
              torch.from_numpy(pos).to(self.dev), torch.from_numpy(slots).to(self.dev))
         self._inputs[step] = t
