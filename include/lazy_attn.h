@@ -246,6 +246,27 @@ lazy_status lazy_attn_decode(const lazy_geom* geom, const lazy_pos_desc* pos, co
                              const int32_t* q_pos, int32_t num_reqs, int32_t max_tiles, int64_t total_tiles,
                              void* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* Decode that allocates nothing, for callers that cannot allocate device
+ * memory at call time (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, semantics and kernels
+ * as lazy_attn_decode, without the workspace: the split-K partials go to a
+ * static device array of LAZY_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds for the life of the process (its address is looked
+ * up on the first call on each device).  When a batch's plan would need
+ * more, it runs with fewer, longer splits that fit; a batch whose query
+ * rows (num_reqs x num_q_heads) cannot fit even two splits' partials is
+ * refused with LAZY_ERR_WORKSPACE.  The scratch keeps the last call's
+ * contents and every call on a device shares it: calls that overlap on one
+ * GPU (different streams, different threads) race and must be serialised
+ * by the caller.  No hipMalloc, hipFree or allocating library routine is
+ * called. */
+#define LAZY_NOALLOC_SCRATCH_BYTES (64u << 20)
+lazy_status lazy_attn_decode_noalloc(const lazy_geom* geom, const lazy_pos_desc* pos, const void* k_cache,
+                                     const void* v_cache, int64_t num_blocks, const uint64_t* tiles,
+                                     const int32_t* tile_start, const int32_t* ctx_tiles, const void* q,
+                                     const int32_t* q_pos, int32_t num_reqs, int32_t max_tiles, int64_t total_tiles,
+                                     void* out, void* stream);
+
 /* Test hook: run the attention kernels' own device-side word unpack on n
  * device words; write device int32 block[n], offset[n], mask[n]. */
 lazy_status lazy_debug_unpack(const uint64_t* words, int64_t n, int32_t* block, int32_t* offset, int32_t* mask,

@@ -33,6 +33,7 @@
 //     writes (m, l, acc) partials when more than one split is used.
 //   * Masked slots are selected to -inf (never multiplied) and their V
 //     values to 0, so garbage in unused slots of partial blocks cannot leak.
+#include <mutex>
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -317,6 +318,23 @@ size_t ws_bytes_for(const lazy_geom* g, const Plan& p) {
   return (size_t)p.splits * (size_t)p.rows_bound * per * sizeof(float) + 256;
 }
 
+// Largest split count whose partials fit `cap` bytes (0 if not even two do).
+int splits_within(const lazy_geom* g, const Plan& p, size_t cap) {
+  const size_t per_split = (size_t)p.rows_bound * ((size_t)g->head_dim + 2) * sizeof(float);
+  if (cap < 256 + 2 * per_split) return 0;
+  return (int)std::min<size_t>((cap - 256) / per_split, 1 << 20);
+}
+
+// The same plan with fewer, longer splits so that its partials fit `cap`
+// bytes (fewer splits only lengthen each wave's tile range).
+void cap_splits(Plan& p, int max_splits, int max_tiles) {
+  if (p.splits <= max_splits) return;
+  long chunk = ((long)max_tiles + max_splits - 1) / max_splits;
+  chunk = (chunk + 1) & ~1L;  // whole tile pairs
+  p.chunk = (int)chunk;
+  p.splits = std::max(1, (int)((max_tiles + chunk - 1) / chunk));
+}
+
 template <typename T, int DH, int KIND, bool DEFER, int RB>
 hipError_t launch_decode(const AttnArgs& a, const Plan& p, int num_reqs, int hkv, hipStream_t st) {
   dim3 grid((unsigned)hkv, (unsigned)num_reqs, (unsigned)((p.splits + kDecodeWT - 1) / kDecodeWT));
@@ -501,18 +519,41 @@ extern "C" lazy_status lazy_attn_prefill(const lazy_geom* geom, const lazy_pos_d
   return LAZY_OK;
 }
 
-extern "C" lazy_status lazy_attn_decode(const lazy_geom* geom, const lazy_pos_desc* pos, const void* k_cache,
-                                        const void* v_cache, int64_t num_blocks, const uint64_t* tiles,
-                                        const int32_t* tile_start, const int32_t* ctx_tiles, const void* q,
-                                        const int32_t* q_pos, int32_t num_reqs, int32_t max_tiles,
-                                        int64_t total_tiles, void* out,
-                                        void* workspace, size_t ws_bytes, void* stream) {
-  clear_error();
+namespace lazy {
+namespace {
+
+// The decode plan; with scratch_cap > 0 its partials must fit that many
+// bytes (fewer, longer splits when the default plan needs more; refused when
+// not even two splits fit).  Host only.
+lazy_status plan_decode(const lazy_geom* geom, int32_t num_reqs, int32_t max_tiles, int64_t total_tiles,
+                        size_t scratch_cap, Plan& p) {
+  p = make_plan(geom, num_reqs, 1, max_tiles, total_tiles, false);
+  if (scratch_cap > 0 && ws_bytes_for(geom, p) > scratch_cap) {
+    const int fit = splits_within(geom, p, scratch_cap);
+    if (fit < 2)
+      return fail(LAZY_ERR_WORKSPACE,
+                  "%d query rows need %zu bytes for two splits' partials; the static scratch holds %zu",
+                  p.rows_bound, 2 * (size_t)p.rows_bound * ((size_t)geom->head_dim + 2) * sizeof(float) + 256,
+                  scratch_cap);
+    cap_splits(p, fit, max_tiles);
+  }
+  return LAZY_OK;
+}
+
+// Decode with a caller-given workspace (scratch_cap == 0) or with the
+// library's static scratch (scratch_cap = its size: the plan is capped to fit).
+lazy_status decode_impl(const lazy_geom* geom, const lazy_pos_desc* pos, const void* k_cache, const void* v_cache,
+                        int64_t num_blocks, const uint64_t* tiles, const int32_t* tile_start,
+                        const int32_t* ctx_tiles, const void* q, const int32_t* q_pos, int32_t num_reqs,
+                        int32_t max_tiles, int64_t total_tiles, void* out, void* workspace, size_t ws_bytes,
+                        size_t scratch_cap, void* stream) {
   lazy_status st = common_checks(geom, pos, k_cache, v_cache, num_blocks, tiles, tile_start, ctx_tiles, q, q_pos,
                                  num_reqs, max_tiles, out);
   if (st != LAZY_OK) return st;
   if (num_reqs == 0) return LAZY_OK;
-  const Plan p = make_plan(geom, num_reqs, 1, max_tiles, total_tiles, false);
+  Plan p;
+  st = plan_decode(geom, num_reqs, max_tiles, total_tiles, scratch_cap, p);
+  if (st != LAZY_OK) return st;
   const size_t need = ws_bytes_for(geom, p);
   if (need > 0 && (workspace == nullptr || ws_bytes < need))
     return fail(LAZY_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
@@ -546,6 +587,70 @@ extern "C" lazy_status lazy_attn_decode(const lazy_geom* geom, const lazy_pos_de
   const hipError_t e = run<false>(geom, pos, a, p, num_reqs, nullptr, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(LAZY_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return LAZY_OK;
+}
+
+// ------------------------------------------------ static scratch (no-allocation decode)
+//
+// The split-K partials of lazy_attn_decode_noalloc live in this file-scope
+// device array: every GPU the library runs on holds its own copy for the
+// life of the process.  Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in symbol): its device address is looked
+// up once per device, with that device current, and kept here.
+static __device__ __align__(256) unsigned char scratch[LAZY_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+lazy_status scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LAZY_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LAZY_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(LAZY_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LAZY_OK;
+}
+
+}  // namespace
+}  // namespace lazy
+
+extern "C" lazy_status lazy_attn_decode(const lazy_geom* geom, const lazy_pos_desc* pos, const void* k_cache,
+                                        const void* v_cache, int64_t num_blocks, const uint64_t* tiles,
+                                        const int32_t* tile_start, const int32_t* ctx_tiles, const void* q,
+                                        const int32_t* q_pos, int32_t num_reqs, int32_t max_tiles,
+                                        int64_t total_tiles, void* out,
+                                        void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  return decode_impl(geom, pos, k_cache, v_cache, num_blocks, tiles, tile_start, ctx_tiles, q, q_pos, num_reqs,
+                     max_tiles, total_tiles, out, workspace, ws_bytes, 0, stream);
+}
+
+extern "C" lazy_status lazy_attn_decode_noalloc(const lazy_geom* geom, const lazy_pos_desc* pos, const void* k_cache,
+                                                const void* v_cache, int64_t num_blocks, const uint64_t* tiles,
+                                                const int32_t* tile_start, const int32_t* ctx_tiles, const void* q,
+                                                const int32_t* q_pos, int32_t num_reqs, int32_t max_tiles,
+                                                int64_t total_tiles, void* out, void* stream) {
+  clear_error();
+  // arguments first: nothing touches the device for a call that would be refused
+  lazy_status st = common_checks(geom, pos, k_cache, v_cache, num_blocks, tiles, tile_start, ctx_tiles, q, q_pos,
+                                 num_reqs, max_tiles, out);
+  if (st != LAZY_OK || num_reqs == 0) return st;
+  Plan p;
+  st = plan_decode(geom, num_reqs, max_tiles, total_tiles, LAZY_NOALLOC_SCRATCH_BYTES, p);  // refusals first
+  if (st != LAZY_OK) return st;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != LAZY_OK) return st;
+  return decode_impl(geom, pos, k_cache, v_cache, num_blocks, tiles, tile_start, ctx_tiles, q, q_pos, num_reqs,
+                     max_tiles, total_tiles, out, ws, LAZY_NOALLOC_SCRATCH_BYTES, LAZY_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 extern "C" lazy_status lazy_debug_unpack(const uint64_t* words, int64_t n, int32_t* block, int32_t* offset,

@@ -33,7 +33,7 @@ EXPORTED = [
     "lazy_rope_freqs", "lazy_softmax_scale", "lazy_rope_table", "lazy_alibi_slopes", "lazy_pack_tiles",
     "lazy_unpack_tiles",
     "lazy_build_tiles", "lazy_kv_write", "lazy_attn_workspace_size", "lazy_attn_prefill", "lazy_attn_decode",
-    "lazy_debug_unpack", "lazy_last_error",
+    "lazy_attn_decode_noalloc", "lazy_debug_unpack", "lazy_last_error",
 ]
 
 
@@ -74,6 +74,7 @@ def lib() -> C.CDLL:
             "lazy_kv_write": [P, P, P, P, I64, P, P, P, P, P, I32, P],
             "lazy_attn_prefill": [P, P, P, P, I64, P, P, P, P, P, P, I32, I32, I32, I64, P, P, C.c_size_t, P],
             "lazy_attn_decode": [P, P, P, P, I64, P, P, P, P, P, I32, I32, I64, P, P, C.c_size_t, P],
+            "lazy_attn_decode_noalloc": [P, P, P, P, I64, P, P, P, P, P, I32, I32, I64, P, P],
             "lazy_debug_unpack": [P, I64, P, P, P, P],
         }
         for name, args in sig.items():
@@ -217,6 +218,17 @@ def attn_decode(geom: Geom, pos: PosDescC, k_cache, v_cache, num_blocks: int, ti
     _check(lib().lazy_attn_decode(C.byref(geom), C.byref(pos), _dev(k_cache), _dev(v_cache), num_blocks, _dev(tiles),
                                   _dev(tile_start), _dev(ctx_tiles), _dev(q), _dev(q_pos), num_reqs, max_tiles,
                                   total_tiles, _dev(out), _dev(workspace), ws_bytes, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LAZY_NOALLOC_SCRATCH_BYTES
+
+
+def attn_decode_noalloc(geom: Geom, pos: PosDescC, k_cache, v_cache, num_blocks: int, tiles, tile_start, ctx_tiles, q,
+                        q_pos, num_reqs: int, max_tiles: int, total_tiles: int, out, stream=None):
+    """lazy_attn_decode without a workspace: split partials in the library's static device scratch."""
+    _check(lib().lazy_attn_decode_noalloc(C.byref(geom), C.byref(pos), _dev(k_cache), _dev(v_cache), num_blocks,
+                                          _dev(tiles), _dev(tile_start), _dev(ctx_tiles), _dev(q), _dev(q_pos),
+                                          num_reqs, max_tiles, total_tiles, _dev(out), _stream(stream)))
 
 
 def debug_unpack(words, block, offset, mask, stream=None):

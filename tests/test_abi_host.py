@@ -239,3 +239,14 @@ def test_device_calls_validate_before_launch(L):
                              None) == L.LAZY_ERR_ARG
     assert lib.lazy_kv_write(C.byref(g), C.byref(p), fake, fake, 10, fake, fake, None, fake, fake, 0, None) == L.LAZY_OK
     assert lib.lazy_debug_unpack(None, -1, None, None, None, None) == L.LAZY_ERR_ARG
+    # the no-allocation decode: same argument checks, an empty batch is a no-op, and a batch whose
+    # partials cannot fit the static scratch even at two splits is refused before any device call
+    def noalloc(geom, pos, nreq, max_tiles, total):
+        return lib.lazy_attn_decode_noalloc(C.byref(geom), C.byref(pos), fake, fake, 10, fake, fake, fake, fake,
+                                            fake, nreq, max_tiles, total, fake, None)
+
+    assert noalloc(L.make_geom(30, 8, 128, "bf16"), p, 4, 64, 0) == L.LAZY_ERR_ARG
+    assert noalloc(g, L.PosDescC(0, 0, 10, -1.0, 1, None, None), 4, 64, 0) == L.LAZY_ERR_ARG
+    assert noalloc(g, p, 0, 64, 0) == L.LAZY_OK
+    assert noalloc(g, p, 4096, 20000, 4096 * 100) == L.LAZY_ERR_WORKSPACE
+    assert "static scratch" in L.last_error()
