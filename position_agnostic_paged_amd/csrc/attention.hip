@@ -258,7 +258,16 @@ constexpr int kPrefillWR = 4;  // waves per prefill workgroup (each RB x 16 quer
 // (two) / 812 (four) / 862 (eight); near-uniform no-sharing batch unchanged
 constexpr int kDecodeWT = 1;
 
-int decode_rb(int group) { return group <= 16 ? 1 : group <= 32 ? 2 : group <= 64 ? 4 : 8; }
+// 16-row blocks per decode wave: the smallest count that holds the G query
+// heads of a KV head (Falcon's MQA 71 heads: 5 blocks, 80 rows, instead of
+// 128 rows of which 57 would be padding)
+int decode_rb(int group) {
+#if LAZY_DECODE_RB_EXACT
+  return group <= 16 ? 1 : group <= 32 ? 2 : group <= 48 ? 3 : group <= 64 ? 4 : group <= 80 ? 5 : 8;
+#else
+  return group <= 16 ? 1 : group <= 32 ? 2 : group <= 64 ? 4 : 8;
+#endif
+}
 
 struct Plan {
   int rb, wr, wt;
@@ -347,6 +356,14 @@ hipError_t launch_decode(const AttnArgs& a, const Plan& p, int num_reqs, int hkv
       return hipGetLastError();
     }
   }
+  // several row blocks of dh 64 (large query groups, MQA): capped at two
+  // waves per SIMD, which the uncapped build's 300+ registers would not
+  // allow (at dh 128 the cap spills hundreds of registers: not used)
+  if constexpr (RB >= 3 && DH == 64 && LAZY_DECODE_MANY_ROWS_WPE > 1) {
+    hipLaunchKernelGGL((decode_kernel<T, DH, KIND, DEFER, RB, kDecodeWT, LAZY_DECODE_MANY_ROWS_WPE>), grid,
+                       dim3(64 * kDecodeWT), 0, st, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((decode_kernel<T, DH, KIND, DEFER, RB, kDecodeWT, 1>), grid, dim3(64 * kDecodeWT), 0, st, a);
   return hipGetLastError();
 }
@@ -371,8 +388,12 @@ hipError_t dispatch_rb(const AttnArgs& a, const Plan& p, int num_reqs, int hkv, 
       return launch_decode<T, DH, KIND, DEFER, 1>(a, p, num_reqs, hkv, st);
     case 2:
       return launch_decode<T, DH, KIND, DEFER, 2>(a, p, num_reqs, hkv, st);
+    case 3:
+      return launch_decode<T, DH, KIND, DEFER, 3>(a, p, num_reqs, hkv, st);
     case 4:
       return launch_decode<T, DH, KIND, DEFER, 4>(a, p, num_reqs, hkv, st);
+    case 5:
+      return launch_decode<T, DH, KIND, DEFER, 5>(a, p, num_reqs, hkv, st);
     default:
       return launch_decode<T, DH, KIND, DEFER, 8>(a, p, num_reqs, hkv, st);
   }

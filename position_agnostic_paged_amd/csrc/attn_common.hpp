@@ -41,6 +41,16 @@
 #ifndef LAZY_UNIFORM_WAVE
 #define LAZY_UNIFORM_WAVE 0
 #endif
+// Decode row blocks per wave: 1 = the smallest count of 16-row blocks that
+// holds a KV head's query group (3 and 5 included), 0 = powers of two only.
+#ifndef LAZY_DECODE_RB_EXACT
+#define LAZY_DECODE_RB_EXACT 1
+#endif
+// Waves per SIMD the dh-64 decode builds with three or more row blocks are
+// register-capped for (1 = no cap).
+#ifndef LAZY_DECODE_MANY_ROWS_WPE
+#define LAZY_DECODE_MANY_ROWS_WPE 2
+#endif
 // Online softmax: rescale only when a row max grows by more than 2^SLACK.
 #ifndef LAZY_RESCALE_SLACK
 #define LAZY_RESCALE_SLACK 8
@@ -71,7 +81,27 @@ struct AttnArgs {
   int32_t hq, hkv, group;
   int32_t rows_bound;  // partial row stride: (max query rows) * hq
   int32_t max_q_len;   // prefill: rows per request covered by the grid
+  int32_t force_partials;  // write (m, l, acc) partials even with one split (a later combine merges more)
 };
+
+// The document-major pass of a decode batch: each shared document's tiles
+// (cached at local positions; tile offset = local position of slot 0) and
+// the reads of it, one per (request, placement).  Read word: request
+// [63:48] | partial slot of that request [47:32] | Delta [31:0].
+struct DocPassArgs {
+  const uint64_t* doc_tiles;
+  const int32_t* doc_tile_start;  // [num_docs + 1]
+  const int32_t* read_start;      // [num_docs + 1]
+  const uint64_t* reads;          // [num_reads]
+  const int32_t* work;            // [num_work][2]: (doc, first 16-row block)
+  int32_t slot_base;              // partial slot of a request's read k = slot_base + k
+};
+
+__device__ __forceinline__ void unpack_read(uint64_t w, int& req, int& slot, int& delta) {
+  req = (int)(w >> 48);
+  slot = (int)((w >> 32) & 0xFFFFull);
+  delta = (int)(w & 0xFFFFFFFFull);
+}
 
 enum { kHalf = LAZY_ROPE_HALF, kInter = LAZY_ROPE_INTERLEAVED, kAlibi = LAZY_ALIBI };
 
@@ -170,6 +200,55 @@ __device__ __forceinline__ void rotate_query(typename Elem<T>::Frag8 (&qr)[RB][D
   }
 }
 
+// q' = R_{-delta_b} q for each row block b with a delta of its own per lane
+// row (the document-major pass: every row is one request's read of the same
+// document at that request's offset).  Same pairing as rotate_query.
+template <typename T, int DH, int KIND, int RB>
+__device__ __forceinline__ void rotate_query_rows(typename Elem<T>::Frag8 (&qr)[RB][DH / 32],
+                                                  const T* const (&qptr)[RB], const AttnArgs& a,
+                                                  const int (&delta)[RB], int g, int active_blocks) {
+  using E = Elem<T>;
+  constexpr int NC = DH / 32;
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    if (b >= active_blocks) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) qr[b][c][t] = E::from_f(0.f);
+      continue;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qr[b][c] = load8<T>(qptr[b] + 32 * c + 8 * g);
+    if (KIND == kAlibi) continue;
+    if (KIND == kHalf) {
+#pragma unroll
+      for (int c = 0; c < NC / 2; ++c) {
+        float cs[8], sn[8];
+        chunk_coefs<DH, KIND>(a, delta[b], g, c, cs, sn);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float x1 = E::to_f(qr[b][c][t]), x2 = E::to_f(qr[b][c + NC / 2][t]);
+          qr[b][c][t] = E::from_f(x1 * cs[t] + x2 * sn[t]);
+          qr[b][c + NC / 2][t] = E::from_f(x2 * cs[t] - x1 * sn[t]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        float cs[8], sn[8];
+        chunk_coefs<DH, KIND>(a, delta[b], g, c, cs, sn);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float x1 = E::to_f(qr[b][c][2 * u]), x2 = E::to_f(qr[b][c][2 * u + 1]);
+          qr[b][c][2 * u] = E::from_f(x1 * cs[u] + x2 * sn[u]);
+          qr[b][c][2 * u + 1] = E::from_f(x2 * cs[u] - x1 * sn[u]);
+        }
+      }
+    }
+  }
+}
+
 // Per-wave attention state: RB blocks of 16 query rows of one (request, KV
 // head) against a stream of tile pairs.  Shared by the prefill and decode
 // kernels.  Query row rho of a request is (token rho / G, head kvh*G + rho % G).
@@ -204,6 +283,7 @@ struct WaveAttn {
   bool rvalid[RB];
   float slope2[RB];
   F8 qr[NQ][RB][NC];
+  int pslot[RB];  // partial slot of each row (-1: the wave's split)
   int cur_delta[2];
   f32x4 acc[RB][NV];
   float m_run[RB], l_run[RB];
@@ -236,6 +316,51 @@ struct WaveAttn {
 #pragma unroll
         for (int c = 0; c < NC; ++c) qr[NQ - 1][b][c] = qr[0][b][c];
     }
+    cur_delta[0] = cur_delta[1] = 0;
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      pslot[b] = -1;
+      m_run[b] = -INFINITY;
+      l_run[b] = 0.f;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) acc[b][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // Document-major pass: the wave's rows are reads of one shared document,
+  // row rho = (read rho / G, head kvh * G + rho % G); each read's query is
+  // rotated once by -Delta of that read, the document's keys stay at their
+  // local positions, and every row's partial goes to its request's slot.
+  struct DocRows {};
+  __device__ __forceinline__ WaveAttn(const AttnArgs& a_, const DocPassArgs& d, int lane, int kvh_, int doc, int nrows,
+                                      int rb0, DocRows)
+      : a(a_) {
+    r = lane & 15;
+    g = lane >> 4;
+    kvh = kvh_;
+    t0 = d.doc_tile_start[doc];
+    nctx = d.doc_tile_start[doc + 1] - t0;  // every tile is a context tile
+    active_blocks = min(RB, (nrows - rb0 * 16 + 15) / 16);
+    const int read0 = d.read_start[doc];
+    int delta[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const int rho = (rb0 + b) * 16 + r;
+      rvalid[b] = rho < nrows;
+      const int rr = rvalid[b] ? rho : 0;
+      int req, slot;
+      unpack_read(d.reads[read0 + rr / a.group], req, slot, delta[b]);
+      const int head = kvh * a.group + rr % a.group;
+      qptr[b] = reinterpret_cast<const T*>(a.q) + ((int64_t)req * a.hq + head) * DH;
+      // ALiBi: the key at local position j sits at Delta + j, so the query's
+      // distance is measured from q_pos - Delta
+      qp[b] = a.q_pos[req] - delta[b];
+      orow[b] = req * a.hq + head;
+      pslot[b] = d.slot_base + slot;
+      slope2[b] = (KIND == kAlibi) ? a.slopes[head] * kLog2e : 0.f;
+      if (KIND == kAlibi) delta[b] = 0;
+    }
+    rotate_query_rows<T, DH, KIND, RB>(qr[0], qptr, a, delta, g, active_blocks);
     cur_delta[0] = cur_delta[1] = 0;
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
@@ -411,7 +536,7 @@ struct WaveAttn {
       if (b >= active_blocks) continue;
       const float l_tot = xor_sum16_32(l_run[b]);
       if (!rvalid[b]) continue;
-      if (a.num_splits == 1) {
+      if (a.num_splits == 1 && !a.force_partials && pslot[b] < 0) {
         const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
         T* o = reinterpret_cast<T*>(a.out) + (int64_t)orow[b] * DH + 4 * g;
 #pragma unroll
@@ -422,7 +547,7 @@ struct WaveAttn {
           *reinterpret_cast<F4*>(o + 16 * n) = w;
         }
       } else {
-        const int64_t prow = (int64_t)split * a.rows_bound + orow[b];
+        const int64_t prow = (int64_t)(pslot[b] >= 0 ? pslot[b] : split) * a.rows_bound + orow[b];
         float* po = a.part_o + prow * DH + 4 * g;
 #pragma unroll
         for (int n = 0; n < NV; ++n) *reinterpret_cast<f32x4*>(po + 16 * n) = acc[b][n];
