@@ -246,6 +246,65 @@ lazy_status lazy_attn_decode(const lazy_geom* geom, const lazy_pos_desc* pos, co
                              const int32_t* q_pos, int32_t num_reqs, int32_t max_tiles, int64_t total_tiles,
                              void* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* Plan of a document-major decode (host; pure).  Input: the batch's segments
+ * as for lazy_build_tiles.  A cached document read by >= min_readers (>= 2)
+ * context segments of the batch (one physical copy: same blocks wherever it
+ * is read) is "shared": it gets one tile list at its local positions (tile
+ * offset = local position of slot 0), and each of its reads a 64-bit read
+ * word: request [63:48] | slot [47:32] | Delta [31:0] (slot = index of the
+ * read among its request's shared reads; Delta = the document's start in
+ * that request, < max_pos when max_pos > 0 for RoPE kinds).  Every request
+ * keeps a tile list of its unshared documents and private tokens (same
+ * layout as lazy_build_tiles).  Work items: (document, first 16-row block,
+ * chunk, tiles per chunk) covering reads x (num_q_heads / num_kv_heads) rows
+ * per document, row_blocks x 16 rows each, and the document's tiles in
+ * chunks (one per document unless the pass would hold fewer than 1024
+ * waves; then up to ceil(2048 / waves) even chunks of >= 32 tiles); a read
+ * takes one partial slot per chunk of its document, from its slot field on.
+ * Outputs (caller-allocated): tiles_out[tiles_cap], tile_start[R+1],
+ * ctx_tiles[R]; doc_tiles_out[doc_tiles_cap]; doc_tile_start, read_start
+ * [docs_cap+1]; reads_out[reads_cap]; req_reads[R] (shared-read slots per
+ * request); work_out[4*work_cap]; counts_out[8] = {documents, reads, work
+ * items, max reads of one request, remaining tiles, max remaining tiles of
+ * one request, document tiles, row_blocks}.  LAZY_ERR_ARG on a capacity too
+ * small or a field out of range. */
+lazy_status lazy_build_shared_plan(const lazy_geom* geom, int32_t kind, int32_t num_reqs, const int32_t* seg_start,
+                                   const int32_t* seg_len, const int64_t* seg_pos0, const uint8_t* seg_is_ctx,
+                                   const int32_t* seg_block_start, const int32_t* blocks, int64_t num_blocks,
+                                   int32_t max_pos, int32_t min_readers, uint64_t* tiles_out, int64_t tiles_cap,
+                                   int32_t* tile_start, int32_t* ctx_tiles, uint64_t* doc_tiles_out,
+                                   int64_t doc_tiles_cap, int32_t* doc_tile_start, int32_t* read_start,
+                                   int32_t docs_cap, uint64_t* reads_out, int64_t reads_cap, int32_t* req_reads,
+                                   int32_t* work_out, int64_t work_cap, int64_t* counts_out);
+
+/* Bytes of workspace lazy_attn_decode_shared needs (split partials of the
+ * requests' own tiles plus one partial slot per shared read). */
+size_t lazy_attn_decode_shared_workspace_size(const lazy_geom* geom, int32_t num_reqs, int32_t max_tiles,
+                                              int64_t total_tiles, int32_t max_req_reads);
+
+/* Document-major decode ([N] "Key designs": decode rotates the query by the
+ * document offset, once per document; [R] README: one position-agnostic copy
+ * per document serves every request).  Same result as lazy_attn_decode over
+ * each request's full tile list, computed in two passes: (1) each request's
+ * own tiles (tiles / tile_start / ctx_tiles of the plan: unshared documents
+ * and private tokens), split-K as in lazy_attn_decode; (2) every shared
+ * document once per KV head for all its reads together: the query of each
+ * read is rotated once by -Delta of that read (RoPE; ALiBi measures the
+ * key's distance from q_pos - Delta) against the document's keys at their
+ * local positions.  A log-sum-exp combine merges each request's partials.
+ * Device arrays come from lazy_build_shared_plan (row_blocks =
+ * counts_out[7]); q, q_pos, out, cache layouts as for lazy_attn_decode.
+ * Needs position-agnostic documents (LAZY_FLAG_PREROTATED is refused).
+ * workspace: device, >= lazy_attn_decode_shared_workspace_size(). */
+lazy_status lazy_attn_decode_shared(const lazy_geom* geom, const lazy_pos_desc* pos, const void* k_cache,
+                                    const void* v_cache, int64_t num_blocks, const uint64_t* tiles,
+                                    const int32_t* tile_start, const int32_t* ctx_tiles, int32_t max_tiles,
+                                    int64_t total_tiles, const uint64_t* doc_tiles, const int32_t* doc_tile_start,
+                                    const int32_t* read_start, const uint64_t* reads, const int32_t* req_reads,
+                                    const int32_t* work, int32_t num_docs, int32_t num_work, int32_t max_req_reads,
+                                    int32_t row_blocks, const void* q, const int32_t* q_pos, int32_t num_reqs,
+                                    void* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* Decode that allocates nothing, for callers that cannot allocate device
  * memory at call time (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, semantics and kernels

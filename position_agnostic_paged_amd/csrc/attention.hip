@@ -155,6 +155,46 @@ __global__ __launch_bounds__(64 * WT) __attribute__((amdgpu_waves_per_eu(WPE))) 
   w.finalize(split);
 }
 
+// Document-major decode pass: one wave = RB blocks of 16 rows of one shared
+// document for one KV head, a row being one request's read of the document
+// (at that request's offset Delta) x one query head of the group.  The
+// document's tiles are read once for all those rows; each row's query is
+// rotated once, by -Delta of its read, and the keys stay at their local
+// positions (the single relative rotation, applied per reader).  A long
+// document is cut into chunks of tiles, one wave each, so a few documents
+// with many readers still fill the chip.  Every row ends as an (m, l, acc)
+// partial in its request's slot (one per chunk), merged with the request's
+// other partials by the combine.  Grid (KV head, work item): one
+// head per XCD, and a document's row blocks are adjacent work items, so the
+// waves reading one document's head slice share an L2.
+template <typename T, int DH, int KIND, int RB, int WPE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void docpass_kernel(AttnArgs a,
+                                                                                            DocPassArgs d) {
+  using W = WaveAttn<T, DH, KIND, false, false, RB>;
+  const int lane = threadIdx.x & 63;
+  const int kvh = blockIdx.x;
+  const int item = blockIdx.y;
+  const int doc = d.work[4 * item];
+  const int rb0 = d.work[4 * item + 1];
+  const int chunk = d.work[4 * item + 2];
+  const int chunk_tiles = d.work[4 * item + 3];
+  const int nrows = (d.read_start[doc + 1] - d.read_start[doc]) * a.group;
+  if (rb0 * 16 >= nrows || chunk_tiles < 1) return;
+  W w(a, d, lane, kvh, doc, nrows, rb0, chunk, chunk_tiles, typename W::DocRows{});
+  const int nt = w.nctx;
+  const int npairs = (nt + 1) >> 1;
+  uint64_t w0 = 0, w1 = 0;
+  if (npairs > 0) w.fetch_words(0, nt, w0, w1);
+  for (int p = 0; p < npairs; ++p) {
+    const typename W::Pair pr = w.decode_pair(2 * p, nt, w0, w1);
+    if (p + 1 < npairs) w.fetch_words(2 * (p + 1), nt, w0, w1);
+    typename W::Frags f;
+    w.load(pr, f);
+    w.consume(pr, f);
+  }
+  w.finalize(0);
+}
+
 // Split-K combine (flash-decoding): for every output row,
 //   M = max_s m_s,  out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,
 // over the splits its request used.  Splits that saw no visible key carry
@@ -165,7 +205,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ q_start,
                                                       const int32_t* __restrict__ tile_start, int32_t num_reqs,
                                                       int32_t hq, int32_t rows_bound, int32_t max_splits,
-                                                      int32_t chunk) {
+                                                      int32_t chunk, const int32_t* __restrict__ extra_n,
+                                                      int32_t extra_base) {
   // RPB rows per workgroup; per row, TPR threads cover the channels (4 each)
   // and NG groups of them take every NG-th split, so the partial loads of
   // many splits are in flight together (NG = 1 for few splits); the groups'
@@ -200,8 +241,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   // of the others (an empty split, m = -inf, has weight 0).
   float M = -INFINITY, L = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s = grp; s < ns; s += NG) {
-    const int64_t pr = (int64_t)s * rows_bound + row;
+  // the request's split partials, then (document-major decode) its partials
+  // from the shared-document pass in slots extra_base ..
+  const int ne = (extra_n != nullptr) ? extra_n[req] : 0;
+  for (int s = grp; s < ns + ne; s += NG) {
+    const int64_t pr = (int64_t)(s < ns ? s : extra_base + (s - ns)) * rows_bound + row;
     const float ms = part_ml[pr * 2], ls = part_ml[pr * 2 + 1];
     const f32x4 os = *reinterpret_cast<const f32x4*>(part_o + pr * DH + c4);
     const float mn = fmaxf(M, ms);
@@ -415,22 +459,49 @@ hipError_t dispatch_kind(int kind, bool defer, const AttnArgs& a, const Plan& p,
 }
 
 template <typename T, int DH>
-hipError_t launch_combine(const AttnArgs& a, const Plan& p, const int32_t* q_start, int num_reqs, hipStream_t st) {
-  // many splits: one row per workgroup, 256 / (DH/4) split groups; few: rows side by side
+hipError_t launch_combine(const AttnArgs& a, const Plan& p, const int32_t* q_start, int num_reqs, hipStream_t st,
+                          const int32_t* extra_n = nullptr, int extra_base = 0, int max_extra = 0) {
+  // many partials per row: one row per workgroup, 256 / (DH/4) split groups;
+  // few: rows side by side
   constexpr int NGMAX = 256 / (DH / 4);
-  if (p.splits > 4) {
+  if (p.splits + max_extra > 4) {
     dim3 grid((unsigned)p.rows_bound);
     hipLaunchKernelGGL((combine_kernel<T, DH, NGMAX>), grid, dim3(256), 0, st, a.part_o, a.part_ml,
                        reinterpret_cast<T*>(a.out), q_start, a.tile_start, num_reqs, a.hq, p.rows_bound, p.splits,
-                       p.chunk);
+                       p.chunk, extra_n, extra_base);
   } else {
     constexpr int RPB = NGMAX;
     dim3 grid((unsigned)((p.rows_bound + RPB - 1) / RPB));
     hipLaunchKernelGGL((combine_kernel<T, DH, 1>), grid, dim3(256), 0, st, a.part_o, a.part_ml,
                        reinterpret_cast<T*>(a.out), q_start, a.tile_start, num_reqs, a.hq, p.rows_bound, p.splits,
-                       p.chunk);
+                       p.chunk, extra_n, extra_base);
   }
   return hipGetLastError();
+}
+
+// The document pass for one (dtype, head_dim, kind).
+template <typename T, int DH, int KIND>
+hipError_t launch_docpass(const AttnArgs& a, const DocPassArgs& d, int rb, int num_work, int hkv, hipStream_t st) {
+  dim3 grid((unsigned)hkv, (unsigned)num_work);
+  // the row blocks docpass_row_blocks gives: 2 at dh 128, 4 at dh 64 (both
+  // within two waves per SIMD)
+  constexpr int RB = (DH == 128) ? 2 : 4;
+  if (rb != RB) return hipErrorNotSupported;
+  hipLaunchKernelGGL((docpass_kernel<T, DH, KIND, RB, (DH == 64) ? 2 : 1>), grid, dim3(64), 0, st, a, d);
+  return hipGetLastError();
+}
+
+template <typename T, int DH>
+hipError_t docpass_kind(int kind, const AttnArgs& a, const DocPassArgs& d, int rb, int num_work, int hkv,
+                        hipStream_t st) {
+  switch (kind) {
+    case kHalf:
+      return launch_docpass<T, DH, kHalf>(a, d, rb, num_work, hkv, st);
+    case kInter:
+      return launch_docpass<T, DH, kInter>(a, d, rb, num_work, hkv, st);
+    default:
+      return launch_docpass<T, DH, kAlibi>(a, d, rb, num_work, hkv, st);
+  }
 }
 
 template <bool PREFILL>
@@ -672,6 +743,120 @@ extern "C" lazy_status lazy_attn_decode_noalloc(const lazy_geom* geom, const laz
   if (st != LAZY_OK) return st;
   return decode_impl(geom, pos, k_cache, v_cache, num_blocks, tiles, tile_start, ctx_tiles, q, q_pos, num_reqs,
                      max_tiles, total_tiles, out, ws, LAZY_NOALLOC_SCRATCH_BYTES, LAZY_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+namespace lazy {
+namespace {
+
+size_t shared_ws_bytes(const lazy_geom* g, const Plan& p, int max_req_reads) {
+  const size_t per = (size_t)g->head_dim + 2;
+  return (size_t)(p.splits + max_req_reads) * (size_t)p.rows_bound * per * sizeof(float) + 256;
+}
+
+template <typename T, int DH>
+hipError_t run_shared(const lazy_pos_desc* pd, const AttnArgs& a, const DocPassArgs& d, const Plan& p, int rb,
+                      int num_work, int num_reqs, int hkv, const int32_t* req_reads, int max_req_reads,
+                      hipStream_t st) {
+  // 1. each request's own tiles (private tokens, unshared documents), split-K
+  //    as usual, always into partials
+  hipError_t e = dispatch_kind<T, DH, false>(pd->kind, true, a, p, num_reqs, hkv, st);
+  if (e != hipSuccess) return e;
+  // 2. every shared document once for all its readers
+  if (num_work > 0) {
+    AttnArgs ad = a;
+    ad.tiles = d.doc_tiles;
+    ad.tile_start = d.doc_tile_start;
+    e = docpass_kind<T, DH>(pd->kind, ad, d, rb, num_work, hkv, st);
+    if (e != hipSuccess) return e;
+  }
+  // 3. per (request, head): the request's split partials and its reads' partials
+  return launch_combine<T, DH>(a, p, nullptr, num_reqs, st, req_reads, d.slot_base, max_req_reads);
+}
+
+}  // namespace
+}  // namespace lazy
+
+extern "C" size_t lazy_attn_decode_shared_workspace_size(const lazy_geom* geom, int32_t num_reqs, int32_t max_tiles,
+                                                        int64_t total_tiles, int32_t max_req_reads) {
+  if (check_geom(geom) != LAZY_OK || num_reqs <= 0 || max_tiles < 0 || max_req_reads < 0) return 0;
+  const Plan p = make_plan(geom, num_reqs, 1, max_tiles, total_tiles, false);
+  return shared_ws_bytes(geom, p, max_req_reads);
+}
+
+extern "C" lazy_status lazy_attn_decode_shared(
+    const lazy_geom* geom, const lazy_pos_desc* pos, const void* k_cache, const void* v_cache, int64_t num_blocks,
+    const uint64_t* tiles, const int32_t* tile_start, const int32_t* ctx_tiles, int32_t max_tiles, int64_t total_tiles,
+    const uint64_t* doc_tiles, const int32_t* doc_tile_start, const int32_t* read_start, const uint64_t* reads,
+    const int32_t* req_reads, const int32_t* work, int32_t num_docs, int32_t num_work, int32_t max_req_reads,
+    int32_t row_blocks, const void* q, const int32_t* q_pos, int32_t num_reqs, void* out, void* workspace,
+    size_t ws_bytes, void* stream) {
+  clear_error();
+  lazy_status st = common_checks(geom, pos, k_cache, v_cache, num_blocks, tiles, tile_start, ctx_tiles, q, q_pos,
+                                 num_reqs, max_tiles, out);
+  if (st != LAZY_OK) return st;
+  if (pos->flags & LAZY_FLAG_PREROTATED)
+    return fail(LAZY_ERR_ARG, "the shared-document decode needs position-agnostic documents (no pre-rotated flag)");
+  if (num_docs < 0 || num_work < 0 || max_req_reads < 0 || max_req_reads > 65536)
+    return fail(LAZY_ERR_ARG, "num_docs, num_work >= 0 and max_req_reads in [0, 65536] required");
+  if (row_blocks != docpass_row_blocks(geom))
+    return fail(LAZY_ERR_ARG, "the plan was built for %d row blocks per wave; this geometry runs %d", row_blocks,
+                docpass_row_blocks(geom));
+  if (num_work > 65535) return fail(LAZY_ERR_UNSUPPORTED, "more than 65535 document work items");
+  if (num_work > 0 && (!doc_tiles || !doc_tile_start || !read_start || !reads || !work))
+    return fail(LAZY_ERR_ARG, "a document-pass array is NULL");
+  if (num_reqs > 0 && !req_reads) return fail(LAZY_ERR_ARG, "req_reads is NULL");
+  if (num_reqs == 0) return LAZY_OK;
+  const Plan p = make_plan(geom, num_reqs, 1, max_tiles, total_tiles, false);
+  const size_t need = shared_ws_bytes(geom, p, max_req_reads);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(LAZY_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  AttnArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_blocks = num_blocks;
+  a.tiles = tiles;
+  a.tile_start = tile_start;
+  a.ctx_tiles = ctx_tiles;
+  a.q = q;
+  a.q_start = nullptr;
+  a.q_pos = q_pos;
+  a.cos_sin = pos->cos_sin;
+  a.inv_freq = pos->inv_freq;
+  a.max_pos = pos->max_pos;
+  a.slopes = pos->alibi_slopes;
+  a.scale_log2 = pos->softmax_scale * kLog2e;
+  a.out = out;
+  a.num_splits = p.splits;
+  a.chunk = p.chunk;
+  a.hq = geom->num_q_heads;
+  a.hkv = geom->num_kv_heads;
+  a.group = geom->num_q_heads / geom->num_kv_heads;
+  a.rows_bound = p.rows_bound;
+  a.max_q_len = 1;
+  a.force_partials = 1;
+  a.part_o = reinterpret_cast<float*>(workspace);
+  a.part_ml = a.part_o + (size_t)(p.splits + max_req_reads) * p.rows_bound * geom->head_dim;
+  DocPassArgs d{};
+  d.doc_tiles = doc_tiles;
+  d.doc_tile_start = doc_tile_start;
+  d.read_start = read_start;
+  d.reads = reads;
+  d.work = work;
+  d.slot_base = p.splits;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int rb = row_blocks, hkv = geom->num_kv_heads;
+  hipError_t e;
+  if (geom->dtype == LAZY_BF16)
+    e = geom->head_dim == 128
+            ? run_shared<bf16, 128>(pos, a, d, p, rb, num_work, num_reqs, hkv, req_reads, max_req_reads, s)
+            : run_shared<bf16, 64>(pos, a, d, p, rb, num_work, num_reqs, hkv, req_reads, max_req_reads, s);
+  else
+    e = geom->head_dim == 128
+            ? run_shared<float, 128>(pos, a, d, p, rb, num_work, num_reqs, hkv, req_reads, max_req_reads, s)
+            : run_shared<float, 64>(pos, a, d, p, rb, num_work, num_reqs, hkv, req_reads, max_req_reads, s);
+  if (e != hipSuccess) return fail(LAZY_ERR_HIP, "shared-document decode launch failed: %s", hipGetErrorString(e));
+  (void)num_docs;
+  return LAZY_OK;
 }
 
 extern "C" lazy_status lazy_debug_unpack(const uint64_t* words, int64_t n, int32_t* block, int32_t* offset,

@@ -93,8 +93,8 @@ struct DocPassArgs {
   const int32_t* doc_tile_start;  // [num_docs + 1]
   const int32_t* read_start;      // [num_docs + 1]
   const uint64_t* reads;          // [num_reads]
-  const int32_t* work;            // [num_work][2]: (doc, first 16-row block)
-  int32_t slot_base;              // partial slot of a request's read k = slot_base + k
+  const int32_t* work;            // [num_work][4]: (doc, first 16-row block, chunk, tiles per chunk)
+  int32_t slot_base;              // partial slots of a request's reads start at slot_base
 };
 
 __device__ __forceinline__ void unpack_read(uint64_t w, int& req, int& slot, int& delta) {
@@ -333,13 +333,18 @@ struct WaveAttn {
   // local positions, and every row's partial goes to its request's slot.
   struct DocRows {};
   __device__ __forceinline__ WaveAttn(const AttnArgs& a_, const DocPassArgs& d, int lane, int kvh_, int doc, int nrows,
-                                      int rb0, DocRows)
+                                      int rb0, int chunk, int chunk_tiles, DocRows)
       : a(a_) {
     r = lane & 15;
     g = lane >> 4;
     kvh = kvh_;
-    t0 = d.doc_tile_start[doc];
-    nctx = d.doc_tile_start[doc + 1] - t0;  // every tile is a context tile
+    // this wave's chunk of the document's tiles (every tile a context tile);
+    // chunk c of a read lands in the read's slot + c
+    const int dt0 = d.doc_tile_start[doc];
+    const int nt_doc = d.doc_tile_start[doc + 1] - dt0;
+    const int tb = min(nt_doc, chunk * chunk_tiles);
+    t0 = dt0 + tb;
+    nctx = min(nt_doc - tb, chunk_tiles);
     active_blocks = min(RB, (nrows - rb0 * 16 + 15) / 16);
     const int read0 = d.read_start[doc];
     int delta[RB];
@@ -356,11 +361,26 @@ struct WaveAttn {
       // distance is measured from q_pos - Delta
       qp[b] = a.q_pos[req] - delta[b];
       orow[b] = req * a.hq + head;
-      pslot[b] = d.slot_base + slot;
+      pslot[b] = d.slot_base + slot + chunk;
       slope2[b] = (KIND == kAlibi) ? a.slopes[head] * kLog2e : 0.f;
       if (KIND == kAlibi) delta[b] = 0;
     }
+    // a Delta the table cannot serve is never looked up: its rows turn NaN
+    bool bad[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      bad[b] = KIND != kAlibi && a.cos_sin != nullptr && (delta[b] < 0 || delta[b] >= a.max_pos);
+      if (bad[b]) delta[b] = 0;
+    }
     rotate_query_rows<T, DH, KIND, RB>(qr[0], qptr, a, delta, g, active_blocks);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      if (!bad[b]) continue;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) qr[0][b][c][t] = E::from_f(__builtin_nanf(""));
+    }
     cur_delta[0] = cur_delta[1] = 0;
 #pragma unroll
     for (int b = 0; b < RB; ++b) {

@@ -18,4 +18,9 @@ lazy_status check_geom(const lazy_geom* g);
 // Positional-descriptor checks (needs_rotation: the call reads cos/sin).
 lazy_status check_pos(const lazy_geom* g, const lazy_pos_desc* p);
 
+// 16-row blocks per wave of the document-major decode pass (rows = reads of
+// one shared document x the query group); the planner and the launch agree
+// through this one function.
+inline int docpass_row_blocks(const lazy_geom* g) { return g->head_dim == 128 ? 2 : 4; }
+
 }  // namespace lazy

@@ -161,6 +161,31 @@ class TileTable:
         self.tiles, self.tile_start, self.ctx_tiles = (views[i] for i in ids)
 
 
+class SharedPlan:
+    """Device copy of a document-major decode plan (lazy_build_shared_plan): each request's own tiles, every
+    shared document's tiles and reads, and the document pass's work items."""
+
+    DEVICE = ("tiles", "tile_start", "ctx_tiles", "doc_tiles", "doc_tile_start", "read_start", "reads", "req_reads",
+              "work")
+
+    def __init__(self, layouts: Sequence[RequestLayout], engine: "Engine", min_readers: int = 2):
+        f = flatten_layouts(layouts)
+        h = L.build_shared_plan(engine.geom, engine.pos.kind_id, f["seg_start"], f["seg_len"], f["seg_pos0"],
+                                f["seg_is_ctx"], f["seg_block_start"], f["blocks"], engine.num_blocks,
+                                engine.pos.table_rows, min_readers)
+        self.host = h
+        self.num_reqs = len(layouts)
+        for k in ("num_docs", "num_reads", "num_work", "max_req_reads", "total_tiles", "max_tiles", "row_blocks"):
+            setattr(self, k, int(h[k]))
+        for k in self.DEVICE:
+            a = h[k]
+            if a.dtype == np.uint64:
+                a = a.view(np.int64)
+            if a.size == 0:
+                a = np.zeros(2, a.dtype)
+            setattr(self, k, torch.from_numpy(np.ascontiguousarray(a)).to(engine.device))
+
+
 class Engine:
     def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str, pos: PosDesc,
                  num_blocks: int, device="cuda", budget_blocks: Optional[int] = None, position_aware: bool = False):
@@ -319,6 +344,34 @@ class Engine:
         L.attn_prefill(self.geom, self.pos.c if pos is None else pos, self.k_cache, self.v_cache, self.num_blocks,
                        tt.tiles, tt.tile_start, tt.ctx_tiles, q, q_start, q_pos0, tt.num_reqs, max_q_len, tt.max_tiles,
                        tt.total_tiles, out, ws, stream)
+        return out
+
+    @property
+    def doc_major_pays(self) -> bool:
+        """Whether the document-major decode is the faster one for this geometry: with a query group of up to
+        16 heads a wave's row blocks hold several reads of a shared document, so its tiles are read once for
+        all of them.  A larger group (Falcon's 71 heads per KV head) fills a wave's rows with one read, the
+        pass then shares nothing and only adds partials (measured on MI355X: 128 x 16K MQA decode 0.141 ms per
+        request vs 0.241 ms document-major; 48 x 8K-66K GQA-8 decode 0.81 vs 0.38 ms)."""
+        return self.hq // self.hkv <= 16
+
+    def shared_plan(self, layouts: Sequence[RequestLayout], min_readers: int = 2) -> SharedPlan:
+        """Plan of a document-major decode: documents read by >= min_readers segments of the batch go through
+        the document pass, the rest through the requests' own tile lists."""
+        return SharedPlan(layouts, self, min_readers)
+
+    def decode_shared(self, plan: SharedPlan, q: torch.Tensor, q_pos: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+        """Decode with every shared document read once for all its readers (lazy_attn_decode_shared)."""
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self._workspace(L.decode_shared_workspace_size(self.geom, plan.num_reqs, plan.max_tiles, plan.total_tiles,
+                                                            plan.max_req_reads))
+        L.attn_decode_shared(self.geom, self.pos.c, self.k_cache, self.v_cache, self.num_blocks, plan.tiles,
+                             plan.tile_start, plan.ctx_tiles, plan.max_tiles, plan.total_tiles, plan.doc_tiles,
+                             plan.doc_tile_start, plan.read_start, plan.reads, plan.req_reads, plan.work,
+                             plan.num_docs, plan.num_work, plan.max_req_reads, plan.row_blocks, q, q_pos,
+                             plan.num_reqs, out, ws, stream)
         return out
 
     def decode(self, tt: TileTable, q: torch.Tensor, q_pos: torch.Tensor, out: Optional[torch.Tensor] = None,

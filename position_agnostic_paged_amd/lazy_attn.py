@@ -33,7 +33,8 @@ EXPORTED = [
     "lazy_rope_freqs", "lazy_softmax_scale", "lazy_rope_table", "lazy_alibi_slopes", "lazy_pack_tiles",
     "lazy_unpack_tiles",
     "lazy_build_tiles", "lazy_kv_write", "lazy_attn_workspace_size", "lazy_attn_prefill", "lazy_attn_decode",
-    "lazy_attn_decode_noalloc", "lazy_debug_unpack", "lazy_last_error",
+    "lazy_attn_decode_noalloc", "lazy_build_shared_plan", "lazy_attn_decode_shared_workspace_size",
+    "lazy_attn_decode_shared", "lazy_debug_unpack", "lazy_last_error",
 ]
 
 
@@ -76,6 +77,10 @@ def lib() -> C.CDLL:
             "lazy_attn_decode": [P, P, P, P, I64, P, P, P, P, P, I32, I32, I64, P, P, C.c_size_t, P],
             "lazy_attn_decode_noalloc": [P, P, P, P, I64, P, P, P, P, P, I32, I32, I64, P, P],
             "lazy_debug_unpack": [P, I64, P, P, P, P],
+            "lazy_build_shared_plan": [P, I32, I32, P, P, P, P, P, P, I64, I32, I32, P, I64, P, P, P, I64, P, P,
+                                       I32, P, I64, P, P, I64, P],
+            "lazy_attn_decode_shared": [P, P, P, P, I64, P, P, P, I32, I64, P, P, P, P, P, P, I32, I32, I32, I32, P,
+                                        P, I32, P, P, C.c_size_t, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -83,6 +88,8 @@ def lib() -> C.CDLL:
             f.restype = I32
         L.lazy_attn_workspace_size.argtypes = [P, I32, I32, I32, I64, I32]
         L.lazy_attn_workspace_size.restype = C.c_size_t
+        L.lazy_attn_decode_shared_workspace_size.argtypes = [P, I32, I32, I64, I32]
+        L.lazy_attn_decode_shared_workspace_size.restype = C.c_size_t
         L.lazy_last_error.argtypes = []
         L.lazy_last_error.restype = C.c_char_p
         _lib = L
@@ -218,6 +225,67 @@ def attn_decode(geom: Geom, pos: PosDescC, k_cache, v_cache, num_blocks: int, ti
     _check(lib().lazy_attn_decode(C.byref(geom), C.byref(pos), _dev(k_cache), _dev(v_cache), num_blocks, _dev(tiles),
                                   _dev(tile_start), _dev(ctx_tiles), _dev(q), _dev(q_pos), num_reqs, max_tiles,
                                   total_tiles, _dev(out), _dev(workspace), ws_bytes, _stream(stream)))
+
+
+def build_shared_plan(geom: Geom, kind: int, seg_start, seg_len, seg_pos0, seg_is_ctx, seg_block_start, blocks,
+                      num_blocks: int, max_pos: int = 0, min_readers: int = 2) -> dict:
+    """Host plan of a document-major decode (numpy arrays, trimmed to their used lengths)."""
+    ss = np.ascontiguousarray(seg_start, np.int32)
+    sl = np.ascontiguousarray(seg_len, np.int32)
+    sp = np.ascontiguousarray(seg_pos0, np.int64)
+    sc = np.ascontiguousarray(seg_is_ctx, np.uint8)
+    sb = np.ascontiguousarray(seg_block_start, np.int32)
+    bl = np.ascontiguousarray(blocks if len(blocks) else [0], np.int32)
+    R = ss.shape[0] - 1
+    nseg = int(ss[-1])
+    cap_tiles = max(1, int(sum((int(n) + 15) // 16 for n in sl)))
+    cap_docs = max(1, int(np.sum(sc)))
+    group = geom.num_q_heads // geom.num_kv_heads
+    # work items: per shared document, (chunks <= tiles/32 + 1) x (row blocks <= readers x G / 16 + 1)
+    per_doc = {}
+    for i in np.flatnonzero(sc):
+        if sl[i] > 0:
+            k = (int(bl[sb[i]]), int(sl[i]))
+            per_doc[k] = per_doc.get(k, 0) + 1
+    cap_work = 1 + sum(((n + 15) // 16 // 32 + 1) * ((r * group + 15) // 16 + 1) for (_, n), r in per_doc.items())
+    out = {"tiles": np.empty(cap_tiles, np.uint64), "tile_start": np.empty(R + 1, np.int32),
+           "ctx_tiles": np.empty(max(R, 1), np.int32), "doc_tiles": np.empty(cap_tiles, np.uint64),
+           "doc_tile_start": np.empty(cap_docs + 1, np.int32), "read_start": np.empty(cap_docs + 1, np.int32),
+           "reads": np.empty(cap_docs, np.uint64), "req_reads": np.empty(max(R, 1), np.int32),
+           "work": np.empty(4 * cap_work, np.int32)}
+    counts = np.zeros(8, np.int64)
+    del nseg
+    _check(lib().lazy_build_shared_plan(
+        C.byref(geom), kind, R, _np_ptr(ss), _np_ptr(sl), _np_ptr(sp), _np_ptr(sc), _np_ptr(sb), _np_ptr(bl),
+        num_blocks, max_pos, min_readers, _np_ptr(out["tiles"]), cap_tiles, _np_ptr(out["tile_start"]),
+        _np_ptr(out["ctx_tiles"]), _np_ptr(out["doc_tiles"]), cap_tiles, _np_ptr(out["doc_tile_start"]),
+        _np_ptr(out["read_start"]), cap_docs, _np_ptr(out["reads"]), cap_docs, _np_ptr(out["req_reads"]),
+        _np_ptr(out["work"]), cap_work, _np_ptr(counts)))
+    nd, nr, nw, max_reads, nt, max_tiles, ndt, rb = (int(x) for x in counts)
+    return {"tiles": out["tiles"][:nt].copy(), "tile_start": out["tile_start"], "ctx_tiles": out["ctx_tiles"][:R].copy(),
+            "doc_tiles": out["doc_tiles"][:ndt].copy(), "doc_tile_start": out["doc_tile_start"][: nd + 1].copy(),
+            "read_start": out["read_start"][: nd + 1].copy(), "reads": out["reads"][:nr].copy(),
+            "req_reads": out["req_reads"][:R].copy(), "work": out["work"][: 4 * nw].copy(), "num_docs": nd,
+            "num_reads": nr, "num_work": nw, "max_req_reads": max_reads, "total_tiles": nt, "max_tiles": max_tiles,
+            "row_blocks": rb}
+
+
+def decode_shared_workspace_size(geom: Geom, num_reqs: int, max_tiles: int, total_tiles: int,
+                                 max_req_reads: int) -> int:
+    return int(lib().lazy_attn_decode_shared_workspace_size(C.byref(geom), num_reqs, max_tiles, total_tiles,
+                                                            max_req_reads))
+
+
+def attn_decode_shared(geom: Geom, pos: PosDescC, k_cache, v_cache, num_blocks: int, tiles, tile_start, ctx_tiles,
+                       max_tiles: int, total_tiles: int, doc_tiles, doc_tile_start, read_start, reads, req_reads, work,
+                       num_docs: int, num_work: int, max_req_reads: int, row_blocks: int, q, q_pos, num_reqs: int,
+                       out, workspace, stream=None):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().lazy_attn_decode_shared(
+        C.byref(geom), C.byref(pos), _dev(k_cache), _dev(v_cache), num_blocks, _dev(tiles), _dev(tile_start),
+        _dev(ctx_tiles), max_tiles, total_tiles, _dev(doc_tiles), _dev(doc_tile_start), _dev(read_start), _dev(reads),
+        _dev(req_reads), _dev(work), num_docs, num_work, max_req_reads, row_blocks, _dev(q), _dev(q_pos), num_reqs,
+        _dev(out), _dev(workspace), ws_bytes, _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # LAZY_NOALLOC_SCRATCH_BYTES

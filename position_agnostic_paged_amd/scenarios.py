@@ -190,8 +190,13 @@ class DecodeScenario(_Base):
     """Decode steps of a fixed batch: documents + optional question, then one new token per step."""
 
     def __init__(self, wl, engine: Engine, shared: bool = True, prerotated: bool = False,
-                 prebuild_tables: bool = False, num_steps: Optional[int] = None, aware: bool = False):
+                 prebuild_tables: bool = False, num_steps: Optional[int] = None, aware: bool = False,
+                 doc_major: bool = False):
         super().__init__(wl, engine, shared, prerotated, aware)
+        # doc_major: documents shared by several requests go through the document-major pass
+        self.doc_major = doc_major
+        if doc_major and (prerotated or not shared):
+            raise ValueError("the document-major decode reads shared position-agnostic documents")
         self.num_steps = wl.num_decode_steps if num_steps is None else num_steps
         R = len(wl.decode_reqs)
         self.R = R
@@ -223,7 +228,14 @@ class DecodeScenario(_Base):
         return out
 
     def table(self, step: int):
+        if self.doc_major:
+            return self.eng.shared_plan(self.layouts(step))
         return self.eng.tile_table(self.layouts(step))
+
+    def _attend(self, tt, q, q_pos, stream):
+        if self.doc_major:
+            return self.eng.decode_shared(tt, q, q_pos, out=self.out, stream=stream)
+        return self.eng.decode(tt, q, q_pos, out=self.out, pos=self.eng.pos.with_flags(self.prerotated), stream=stream)
 
     def positions(self, step: int) -> np.ndarray:
         return (self.priv_pos0 + self.pre_len + step).astype(np.int32)
@@ -254,8 +266,7 @@ class DecodeScenario(_Base):
         tt = self.tables[step] if self.tables is not None else self.table(step)
         if events is not None:
             events[0].record()
-        out = self.eng.decode(tt, self.q, pos, out=self.out, pos=self.eng.pos.with_flags(self.prerotated),
-                              stream=stream)
+        out = self._attend(tt, self.q, pos, stream)
         if events is not None:
             events[1].record()
         return out
@@ -267,7 +278,7 @@ class DecodeScenario(_Base):
         tt = self.tables[step] if self.tables is not None else self.table(step)
         if events is not None and events[0] is not None:
             events[0].record()
-        out = self.eng.decode(tt, q, q_pos, out=self.out, pos=self.eng.pos.with_flags(self.prerotated), stream=stream)
+        out = self._attend(tt, q, q_pos, stream)
         if events is not None:
             events[1].record()
         return out

@@ -121,6 +121,59 @@ int main() {
   }
   CHECK(lazy_build_tiles(9, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 1, 0, nullptr, 0, nullptr,
                          nullptr) == LAZY_ERR_ARG);
+
+  // document-major plan: requests drawing documents from a shared pool, generous and short capacities
+  lazy_geom geom{32, 8, 128, 16, LAZY_BF16};
+  for (int trial = 0; trial < 100; ++trial) {
+    const int R = 1 + (int)(rng() % 8), pool = 1 + (int)(rng() % 6);
+    std::vector<int32_t> doc_len(pool), doc_b0(pool);
+    int32_t nb = 0;
+    for (int d = 0; d < pool; ++d) {
+      doc_len[d] = 1 + (int)(rng() % 600);
+      doc_b0[d] = nb;
+      nb += (doc_len[d] + 15) / 16;
+    }
+    std::vector<int32_t> seg_start{0}, seg_len, seg_bs{0}, blocks;
+    std::vector<int64_t> seg_pos0;
+    std::vector<uint8_t> seg_ctx;
+    for (int r = 0; r < R; ++r) {
+      int64_t pos = 0;
+      const int nd = (int)(rng() % 5);
+      for (int k = 0; k < nd; ++k) {
+        const int d = (int)(rng() % pool);
+        seg_len.push_back(doc_len[d]);
+        seg_pos0.push_back(pos);
+        seg_ctx.push_back(1);
+        for (int b = 0; b < (doc_len[d] + 15) / 16; ++b) blocks.push_back(doc_b0[d] + b);
+        seg_bs.push_back((int32_t)blocks.size());
+        pos += doc_len[d];
+      }
+      seg_len.push_back(3);
+      seg_pos0.push_back(pos);
+      seg_ctx.push_back(0);
+      blocks.push_back(nb++);
+      seg_bs.push_back((int32_t)blocks.size());
+      seg_start.push_back((int32_t)seg_len.size());
+    }
+    const int64_t cap = (int64_t)blocks.size() + 1, docs_cap = (int64_t)seg_len.size() + 1;
+    const int64_t work_cap = 4096;
+    std::vector<uint64_t> tiles(cap), dtiles(cap), reads(docs_cap);
+    std::vector<int32_t> tstart(R + 1), nctx(R), dstart(docs_cap + 1), rstart(docs_cap + 1), rreads(R), work(4 * work_cap);
+    std::vector<int64_t> counts(8);
+    for (int shortcap = 0; shortcap < 2; ++shortcap) {
+      const lazy_status st = lazy_build_shared_plan(
+          &geom, trial % 3, R, seg_start.data(), seg_len.data(), seg_pos0.data(), seg_ctx.data(), seg_bs.data(),
+          blocks.data(), nb, 0, 2, tiles.data(), shortcap ? 0 : cap, tstart.data(), nctx.data(), dtiles.data(), cap,
+          dstart.data(), rstart.data(), (int32_t)docs_cap, reads.data(), docs_cap, rreads.data(), work.data(),
+          shortcap ? 0 : work_cap, counts.data());
+      if (shortcap) {
+        CHECK(st == LAZY_ERR_ARG);
+      } else {
+        CHECK(st == LAZY_OK);
+        CHECK(counts[4] <= cap && counts[6] <= cap && counts[1] <= docs_cap && counts[2] <= work_cap);
+      }
+    }
+  }
   printf("host driver: all checks passed\n");
   return 0;
 }

@@ -71,12 +71,17 @@ def check_prefill(key, variants=((True, False, False),), negative=True):
 
 # ------------------------------------------------------------------------------------------- decode
 
-def run_decode(wl, steps, shared=True, prerotated=False, on_the_fly=False, num_steps=None):
-    """GPU decode outputs {step: [R][Hq][dh]} over consecutive steps 0..max(steps)."""
+def run_decode(wl, steps, shared=True, prerotated=False, on_the_fly=False, doc_major=False, num_steps=None):
+    """GPU decode outputs {step: [R][Hq][dh]} over consecutive steps 0..max(steps); doc_major runs the
+    document-major decode (shared documents read once for all their readers)."""
     from position_agnostic_paged_amd.scenarios import DecodeScenario
 
     eng = _engine(wl, shared, on_the_fly=on_the_fly)
-    sc = DecodeScenario(wl, eng, shared=shared, prerotated=prerotated, num_steps=num_steps)
+    sc = DecodeScenario(wl, eng, shared=shared, prerotated=prerotated, num_steps=num_steps, doc_major=doc_major)
+    if doc_major:
+        plan = sc.table(0)
+        say(f"  document-major plan at step 0: {plan.num_docs} shared documents, {plan.num_reads} reads, "
+            f"{plan.num_work} work items, {plan.total_tiles} tiles left to the requests' own lists")
     got = {}
     for s in range(max(steps) + 1):
         out = sc.step(s)
@@ -114,6 +119,8 @@ SHARED = (True, False, False)
 NOSHARE_PREROT = (False, True, False)  # the overhead control: private copies at global positions, no deferral
 NOSHARE = (False, False, False)
 ON_THE_FLY = (True, False, True)
+DOC_MAJOR = (True, False, False, True)  # decode: shared documents once for all their readers
+DOC_MAJOR_FLY = (True, False, True, True)
 
 
 # ---------------------------------------------------------------------------------------- the tests
@@ -123,7 +130,18 @@ def test_tiny_fp32_prefill():
 
 
 def test_tiny_fp32_decode():
-    check_decode("tiny_fp32", steps=list(range(8)), variants=(SHARED, ON_THE_FLY, NOSHARE_PREROT))
+    check_decode("tiny_fp32", steps=list(range(8)), variants=(SHARED, ON_THE_FLY, NOSHARE_PREROT, DOC_MAJOR))
+
+
+def test_tiny_fp32_decode_document_major_two_orders():
+    """fp32 through the document pass: two requests read both documents, in opposite orders (each document
+    at two different offsets), plus their own question tokens."""
+    from workloads.gen import DecodeRequest
+
+    wl = make_workload("tiny_fp32")
+    r0 = wl.decode_reqs[0]
+    wl.decode_reqs = [r0, DecodeRequest(doc_ids=[1, 0], k=r0.k[:9], v=r0.v[:9])]
+    check_decode(wl, steps=[0, 3, 7], variants=(SHARED, DOC_MAJOR, DOC_MAJOR_FLY))
 
 
 def test_llama8b_prefill_and_controls():
@@ -139,7 +157,7 @@ def test_llama8b_prefill_interleaved():
 def test_llama8b_decode_every_request_and_prerotated_control():
     """Config 3 (64 x 32K tokens): every request at steps 0, 31 and 63 of the 64-step run, through the
     shared-document cache and through the no-sharing pre-rotated control the overhead A/B times."""
-    check_decode("llama8b_decode", steps=[0, 31, 63], variants=(SHARED, NOSHARE_PREROT))
+    check_decode("llama8b_decode", steps=[0, 31, 63], variants=(SHARED, NOSHARE_PREROT, DOC_MAJOR))
 
 
 def test_llama8b_decode_sample_every_step():
@@ -154,13 +172,14 @@ def test_llama8b_decode_sharp_queries():
     shared and no-sharing deferred layouts."""
     rng = np.random.default_rng(4)
     reqs = sorted(rng.choice(64, size=12, replace=False).tolist())
-    check_decode(sharpened(make_workload("llama8b_decode")), steps=[0, 63], reqs=reqs, variants=(SHARED, NOSHARE))
+    check_decode(sharpened(make_workload("llama8b_decode")), steps=[0, 63], reqs=reqs,
+                 variants=(SHARED, NOSHARE, DOC_MAJOR))
 
 
 def test_falcon_alibi_decode_every_request():
     """Config 5 (MQA 71/1, dh 64, ALiBi, 128 x 16K): every request at steps 0, 31, 63 of 64, shared
     documents and the no-sharing control."""
-    check_decode("falcon7b_alibi", steps=[0, 31, 63], variants=(SHARED, NOSHARE))
+    check_decode("falcon7b_alibi", steps=[0, 31, 63], variants=(SHARED, NOSHARE, DOC_MAJOR))
 
 
 def test_ragged_prefill():
@@ -171,7 +190,7 @@ def test_ragged_prefill():
 def test_ragged_decode_uneven_splits():
     """Requests from 7 to 11K tokens: per-request split counts differ inside one launch (the three-wave
     build for uneven batches), with its pre-rotated control."""
-    check_decode("ragged", steps=[0, 2, 4], variants=(SHARED, NOSHARE_PREROT))
+    check_decode("ragged", steps=[0, 2, 4], variants=(SHARED, NOSHARE_PREROT, DOC_MAJOR))
 
 
 @pytest.mark.parametrize("on_the_fly", [False, True], ids=["table", "on_the_fly"])
@@ -181,7 +200,8 @@ def test_long_context_offsets_beyond_100k(on_the_fly):
     the tile words, many splits); queries x4 so the outputs depend on where every document sits."""
     v = ON_THE_FLY if on_the_fly else SHARED
     check_prefill(sharpened(make_workload("long_context")), variants=(v,))
-    check_decode(sharpened(make_workload("long_context")), steps=[0, 1], variants=(v,))
+    check_decode(sharpened(make_workload("long_context")), steps=[0, 1],
+                 variants=(v, DOC_MAJOR_FLY if on_the_fly else DOC_MAJOR))
 
 
 def test_mixed_yarn_prefill_and_prerotated_control():
@@ -200,7 +220,7 @@ def test_mixed_yarn_decode_every_request():
 
     wl = gen._mixed_llama70b(num_steps=3)
     wl.prefill_steps = []
-    check_decode(wl, steps=[0, 2])
+    check_decode(wl, steps=[0, 2], variants=(SHARED, DOC_MAJOR))
 
 
 def test_pages_overhead_shape_prefill():
@@ -216,7 +236,7 @@ def test_pages_overhead_shape_decode():
     the no-sharing A/B pair."""
     wl = make_workload("pages_overhead")
     wl.prefill_steps = []
-    check_decode(wl, steps=[0, 3], variants=(SHARED, NOSHARE, NOSHARE_PREROT))
+    check_decode(wl, steps=[0, 3], variants=(SHARED, NOSHARE, NOSHARE_PREROT, DOC_MAJOR))
 
 
 def test_falcon_alibi_prefill_mqa_dh64():
@@ -228,7 +248,7 @@ def test_dh64_interleaved_prefill_decode_and_control():
     """dh 64 interleaved RoPE through the staged prefill (K rotated in LDS), the decode kernel and the
     pre-rotated control on the no-sharing layout."""
     check_prefill("small_dh64_interleaved", variants=(SHARED, NOSHARE_PREROT))
-    check_decode("small_dh64_interleaved", steps=[0, 1, 2, 3], variants=(SHARED, NOSHARE_PREROT))
+    check_decode("small_dh64_interleaved", steps=[0, 1, 2, 3], variants=(SHARED, NOSHARE_PREROT, DOC_MAJOR))
 
 
 def test_uneven_decode_alibi():
@@ -238,7 +258,7 @@ def test_uneven_decode_alibi():
 
     wl = make_workload("ragged")
     wl.pos = PosSpec("alibi")
-    check_decode(wl, steps=[0, 1])
+    check_decode(wl, steps=[0, 1], variants=(SHARED, DOC_MAJOR))
 
 
 def test_documents_in_request_order_without_reuse_ordering():

@@ -44,10 +44,10 @@ def _prefill(wl, poison):
     return out, gate
 
 
-def _decode(wl, poison, steps):
+def _decode(wl, poison, steps, doc_major=False):
     from position_agnostic_paged_amd.scenarios import DecodeScenario
 
-    sc = DecodeScenario(wl, _engine(wl, poison))
+    sc = DecodeScenario(wl, _engine(wl, poison), doc_major=doc_major)
     draws, got = {}, {}
     for s in range(max(steps) + 1):
         draws[s] = wl.decode_step(s)
@@ -55,7 +55,7 @@ def _decode(wl, poison, steps):
         if s in steps:
             got[s] = out.float().cpu().numpy()
     torch.cuda.synchronize()
-    gate = Gate(f"{wl.name} decode poison={poison}", wl.geom.dtype)
+    gate = Gate(f"{wl.name} decode poison={poison} doc_major={doc_major}", wl.geom.dtype)
     for r in range(len(wl.decode_reqs)):
         want = oracle_decode(wl, r, steps, draws)
         for s, w in zip(steps, want):
@@ -75,11 +75,12 @@ def test_nan_poisoned_unused_slots_prefill(key):
     gate.check()
 
 
+@pytest.mark.parametrize("doc_major", [False, True], ids=["per_request", "document_major"])
 @pytest.mark.parametrize("key", ["ragged", "tiny_fp32"])
-def test_nan_poisoned_unused_slots_decode(key):
+def test_nan_poisoned_unused_slots_decode(key, doc_major):
     wl = make_workload(key)
-    say(f"[nan-poisoned decode] {wl.name}")
-    got, gate = _decode(wl, poison=True, steps=[0, 2])
+    say(f"[nan-poisoned decode] {wl.name} doc_major={doc_major}")
+    got, gate = _decode(wl, poison=True, steps=[0, 2], doc_major=doc_major)
     assert all(np.isfinite(g).all() for g in got.values())
     gate.check()
 
@@ -104,6 +105,8 @@ def test_same_document_at_two_offsets_in_one_request():
     say(f"[repeated documents] prefill {[r.doc_ids for r in pre]}, decode {[r.doc_ids for r in decs]}")
     out, gate_p = _prefill(wl, poison=False)
     got, gate_d = _decode(wl, poison=False, steps=[0, 1])
+    got_m, gate_m = _decode(wl, poison=False, steps=[0, 1], doc_major=True)  # read twice by one request: two slots
     assert np.isfinite(out).all()
     gate_p.check()
     gate_d.check()
+    gate_m.check()
