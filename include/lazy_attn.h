@@ -261,6 +261,9 @@ lazy_status lazy_attn_decode(const lazy_geom* geom, const lazy_pos_desc* pos, co
  * chunks (one per document unless the pass would hold fewer than 1024
  * waves; then up to ceil(2048 / waves) even chunks of >= 32 tiles); a read
  * takes one partial slot per chunk of its document, from its slot field on.
+ * (A build with workgroups of several doc-pass waves pads each (document,
+ * chunk)'s items to a multiple of that count with empty items, first row
+ * block past the document's rows.)
  * Outputs (caller-allocated): tiles_out[tiles_cap], tile_start[R+1],
  * ctx_tiles[R]; doc_tiles_out[doc_tiles_cap]; doc_tile_start, read_start
  * [docs_cap+1]; reads_out[reads_cap]; req_reads[R] (shared-read slots per

@@ -168,12 +168,13 @@ __global__ __launch_bounds__(64 * WT) __attribute__((amdgpu_waves_per_eu(WPE))) 
 // head per XCD, and a document's row blocks are adjacent work items, so the
 // waves reading one document's head slice share an L2.
 template <typename T, int DH, int KIND, int RB, int WPE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void docpass_kernel(AttnArgs a,
-                                                                                            DocPassArgs d) {
+__global__ __launch_bounds__(64 * kDocPassWgWaves) __attribute__((amdgpu_waves_per_eu(WPE))) void docpass_kernel(
+    AttnArgs a, DocPassArgs d) {
   using W = WaveAttn<T, DH, KIND, false, false, RB>;
   const int lane = threadIdx.x & 63;
   const int kvh = blockIdx.x;
-  const int item = blockIdx.y;
+  // the workgroup's waves are the row blocks of one (document, chunk)
+  const int item = blockIdx.y * kDocPassWgWaves + (threadIdx.x >> 6);
   const int doc = d.work[4 * item];
   const int rb0 = d.work[4 * item + 1];
   const int chunk = d.work[4 * item + 2];
@@ -359,7 +360,7 @@ Plan make_plan(const lazy_geom* g, int num_reqs, int max_q_len, int max_tiles, i
     p.row_tiles = 1;
     p.uneven = total_tiles > 0 && (double)max_tiles * num_reqs > 1.25 * (double)total_tiles;
     size_splits(p, g->num_kv_heads, num_reqs, max_tiles, total_tiles,
-                p.uneven ? LAZY_DECODE_WAVE_TARGET_UNEVEN : LAZY_DECODE_WAVE_TARGET, 32);
+                p.uneven ? LAZY_DECODE_WAVE_TARGET_UNEVEN : LAZY_DECODE_WAVE_TARGET, LAZY_DECODE_MIN_CHUNK);
     p.rows_bound = num_reqs * g->num_q_heads;
   }
   return p;
@@ -482,12 +483,14 @@ hipError_t launch_combine(const AttnArgs& a, const Plan& p, const int32_t* q_sta
 // The document pass for one (dtype, head_dim, kind).
 template <typename T, int DH, int KIND>
 hipError_t launch_docpass(const AttnArgs& a, const DocPassArgs& d, int rb, int num_work, int hkv, hipStream_t st) {
-  dim3 grid((unsigned)hkv, (unsigned)num_work);
+  if (num_work % kDocPassWgWaves != 0) return hipErrorInvalidValue;  // the plan pads every group
+  dim3 grid((unsigned)hkv, (unsigned)(num_work / kDocPassWgWaves));
   // the row blocks docpass_row_blocks gives: 2 at dh 128, 4 at dh 64 (both
   // within two waves per SIMD)
-  constexpr int RB = (DH == 128) ? 2 : 4;
+  constexpr int RB = (DH == 128) ? LAZY_DOCPASS_RB128 : 4;
   if (rb != RB) return hipErrorNotSupported;
-  hipLaunchKernelGGL((docpass_kernel<T, DH, KIND, RB, (DH == 64) ? 2 : 1>), grid, dim3(64), 0, st, a, d);
+  hipLaunchKernelGGL((docpass_kernel<T, DH, KIND, RB, (DH == 64) ? 2 : 1>), grid, dim3(64 * kDocPassWgWaves), 0, st,
+                     a, d);
   return hipGetLastError();
 }
 
@@ -801,7 +804,10 @@ extern "C" lazy_status lazy_attn_decode_shared(
   if (row_blocks != docpass_row_blocks(geom))
     return fail(LAZY_ERR_ARG, "the plan was built for %d row blocks per wave; this geometry runs %d", row_blocks,
                 docpass_row_blocks(geom));
-  if (num_work > 65535) return fail(LAZY_ERR_UNSUPPORTED, "more than 65535 document work items");
+  if (num_work / kDocPassWgWaves > 65535) return fail(LAZY_ERR_UNSUPPORTED, "too many document work items");
+  if (num_work % kDocPassWgWaves != 0)
+    return fail(LAZY_ERR_ARG, "num_work %d is not a multiple of %d (the plan pads each document's items)", num_work,
+                kDocPassWgWaves);
   if (num_work > 0 && (!doc_tiles || !doc_tile_start || !read_start || !reads || !work))
     return fail(LAZY_ERR_ARG, "a document-pass array is NULL");
   if (num_reqs > 0 && !req_reads) return fail(LAZY_ERR_ARG, "req_reads is NULL");

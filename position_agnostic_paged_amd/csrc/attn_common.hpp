@@ -32,6 +32,10 @@
 #ifndef LAZY_DECODE_WAVE_TARGET_UNEVEN
 #define LAZY_DECODE_WAVE_TARGET_UNEVEN 12288
 #endif
+// Decode: fewest tiles per split.
+#ifndef LAZY_DECODE_MIN_CHUNK
+#define LAZY_DECODE_MIN_CHUNK 16
+#endif
 // Prefill split heuristic: about this many workgroups per launch.
 #ifndef LAZY_PREFILL_WG_TARGET
 #define LAZY_PREFILL_WG_TARGET 256

@@ -428,14 +428,19 @@ extern "C" lazy_status lazy_build_shared_plan(
   // 6. work items of the document pass: (document, first 16-row block,
   //    chunk, tiles per chunk) for every docpass_row_blocks x 16 rows of
   //    reads x query group and every chunk; a document's items adjacent
+  //    Each (document, chunk)'s items are padded to a multiple of
+  //    kDocPassWgWaves with empty items (first row block past the rows) so
+  //    that a workgroup holds one document's row blocks only.
   int64_t nw = 0;
   for (size_t i = 0; i < docs.size(); ++i) {
     const int64_t rows = (int64_t)docs[i].readers * group;
+    const int64_t items = (rows + 16 * rb - 1) / (16 * rb);
+    const int64_t padded = (items + kDocPassWgWaves - 1) / kDocPassWgWaves * kDocPassWgWaves;
     for (int32_t c = 0; c < nchunks[i]; ++c)
-      for (int64_t b0 = 0; b0 * 16 < rows; b0 += rb) {
+      for (int64_t k = 0; k < padded; ++k) {
         if (nw >= work_cap) return fail(LAZY_ERR_ARG, "work_cap %lld too small", (long long)work_cap);
         work_out[4 * nw] = (int32_t)i;
-        work_out[4 * nw + 1] = (int32_t)b0;
+        work_out[4 * nw + 1] = (int32_t)(k < items ? k * rb : (rows + 15) / 16);  // empty: no rows left
         work_out[4 * nw + 2] = c;
         work_out[4 * nw + 3] = chunk_tiles[i];
         ++nw;

@@ -247,7 +247,7 @@ def build_shared_plan(geom: Geom, kind: int, seg_start, seg_len, seg_pos0, seg_i
         if sl[i] > 0:
             k = (int(bl[sb[i]]), int(sl[i]))
             per_doc[k] = per_doc.get(k, 0) + 1
-    cap_work = 1 + sum(((n + 15) // 16 // 32 + 1) * ((r * group + 15) // 16 + 1) for (_, n), r in per_doc.items())
+    cap_work = 1 + sum(((n + 15) // 16 // 32 + 1) * ((r * group + 15) // 16 + 4) for (_, n), r in per_doc.items())
     out = {"tiles": np.empty(cap_tiles, np.uint64), "tile_start": np.empty(R + 1, np.int32),
            "ctx_tiles": np.empty(max(R, 1), np.int32), "doc_tiles": np.empty(cap_tiles, np.uint64),
            "doc_tile_start": np.empty(cap_docs + 1, np.int32), "read_start": np.empty(cap_docs + 1, np.int32),

@@ -86,8 +86,10 @@ def _expected(layouts, kind, num_blocks, group, hkv, rb, min_readers):
     work = []
     for i, k in enumerate(docs):
         rows = readers[k] * group
+        items = -(-rows // (16 * rb))
+        padded = items  # one doc-pass wave per workgroup: no padding
         for c in range(nchunks[k]):
-            work += [(i, b0, c, ct[k]) for b0 in range(0, (rows + 15) // 16, rb)]
+            work += [(i, b * rb if b < items else (rows + 15) // 16, c, ct[k]) for b in range(padded)]
     return {"doc_tiles": doc_tiles, "doc_start": doc_start, "reads": reads, "req_reads": req_reads,
             "tiles": [int(w) for w in tiles], "tile_start": list(tstart), "ctx_tiles": list(nctx), "work": work}
 
