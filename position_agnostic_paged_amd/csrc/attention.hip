@@ -489,7 +489,7 @@ hipError_t launch_docpass(const AttnArgs& a, const DocPassArgs& d, int rb, int n
   // within two waves per SIMD)
   constexpr int RB = (DH == 128) ? LAZY_DOCPASS_RB128 : 4;
   if (rb != RB) return hipErrorNotSupported;
-  hipLaunchKernelGGL((docpass_kernel<T, DH, KIND, RB, (DH == 64) ? 2 : 1>), grid, dim3(64 * kDocPassWgWaves), 0, st,
+  hipLaunchKernelGGL((docpass_kernel<T, DH, KIND, RB, LAZY_DOCPASS_WPE>), grid, dim3(64 * kDocPassWgWaves), 0, st,
                      a, d);
   return hipGetLastError();
 }

@@ -36,6 +36,12 @@
 #ifndef LAZY_DECODE_MIN_CHUNK
 #define LAZY_DECODE_MIN_CHUNK 16
 #endif
+// Document pass: waves per SIMD the build is register-capped for (2 fits its
+// 200 registers without spills; the uncapped build drifts past 256 and runs
+// one wave per SIMD, 0.47 vs 0.37 ms on the mixed step's decode; 3 spills).
+#ifndef LAZY_DOCPASS_WPE
+#define LAZY_DOCPASS_WPE 2
+#endif
 // Prefill split heuristic: about this many workgroups per launch.
 #ifndef LAZY_PREFILL_WG_TARGET
 #define LAZY_PREFILL_WG_TARGET 256
