@@ -114,10 +114,12 @@ def _dev(t) -> Optional[int]:
 
 
 def _stream(stream) -> Optional[int]:
+    """The HIP stream handle of a torch stream (None: the current stream of the current device)."""
     if stream is None:
         import torch
 
-        return torch.cuda.current_stream().cuda_stream
+        # the raw handle of torch's current stream, without building a Stream object per call
+        return torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice())
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 

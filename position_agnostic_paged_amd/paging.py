@@ -68,6 +68,7 @@ class DocCache:
         self.budget = budget_blocks if budget_blocks is not None else pool.num_blocks
         self._docs: "OrderedDict[int, CachedDoc]" = OrderedDict()
         self.used = 0
+        self.unpinned = 0  # blocks of cached entries no work holds (what eviction can free)
         self.hits = 0
         self.misses = 0
         self.evictions = 0
@@ -92,6 +93,8 @@ class DocCache:
             if d.length != length:
                 raise ValueError(f"doc {doc_id} cached with length {d.length}, asked {length}")
             self._docs.move_to_end(doc_id)
+            if d.pins == 0:
+                self.unpinned -= len(d.blocks)
             d.pins += 1
             self.hits += 1
             return d.blocks, True
@@ -108,12 +111,16 @@ class DocCache:
         if d.pins <= 0:
             raise ValueError(f"doc {doc_id} is not pinned")
         d.pins -= 1
+        if d.pins == 0:
+            self.unpinned += len(d.blocks)
 
     def forget(self, doc_id: int) -> None:
         """Drop a document whatever its pins (a miss whose content was never written)."""
         d = self._docs.pop(doc_id)
         self.pool.free(d.blocks)
         self.used -= len(d.blocks)
+        if d.pins == 0:
+            self.unpinned -= len(d.blocks)
 
     def _make_room(self, need: int) -> None:
         room = min(self.budget - self.used, self.pool.free_blocks)
@@ -135,11 +142,12 @@ class DocCache:
             d = self._docs.pop(key)
             self.pool.free(d.blocks)
             self.used -= len(d.blocks)
+            self.unpinned -= len(d.blocks)
             self.evictions += 1
 
     def room_for_private(self, n: int) -> bool:
         """Whether n private blocks fit the budget after evicting every unpinned document."""
-        evictable = sum(len(d.blocks) for d in self._docs.values() if d.pins == 0)
+        evictable = self.unpinned
         return min(self.budget - self.used + evictable, self.pool.free_blocks + evictable) >= n
 
     def take_private(self, n: int) -> List[int]:

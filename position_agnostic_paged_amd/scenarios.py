@@ -217,6 +217,9 @@ class DecodeScenario(_Base):
         self.pre_len = np.asarray(self.pre_len, np.int64)
         self.q = torch.empty((R, wl.geom.num_q_heads, wl.geom.head_dim), dtype=self.tdtype, device=self.dev)
         self.out = torch.empty_like(self.q)
+        self._priv_blocks = None
+        # tokens of each request's cached documents (the bytes accounting of every step)
+        self._ctx_tokens = np.array([sum(sg.length for sg in segs) for segs in self.ctx_segs], np.int64)
         self.tables = [self.table(s) for s in range(self.num_steps)] if prebuild_tables else None
         self._inputs = {}
 
@@ -242,8 +245,14 @@ class DecodeScenario(_Base):
 
     def slots(self, step: int) -> np.ndarray:
         """Slot id of each request's new token at a step."""
-        return np.array([self.eng.slots_for(self.priv[r], 1, int(self.pre_len[r]) + step)[0] for r in range(self.R)],
-                        np.int64)
+        if self._priv_blocks is None:
+            # one row of private block ids per request (padded), so a step's slots are one gather
+            width = max(len(b) for b in self.priv) if self.R else 1
+            self._priv_blocks = np.zeros((self.R, max(width, 1)), np.int64)
+            for r, b in enumerate(self.priv):
+                self._priv_blocks[r, : len(b)] = b
+        i = self.pre_len + step
+        return self._priv_blocks[np.arange(self.R), i // 16] * 16 + i % 16
 
     def stage_inputs(self, step: int):
         """Device copies of the step's raw q/k/v, positions and slots (setup, not timed)."""
@@ -287,5 +296,5 @@ class DecodeScenario(_Base):
         """Algorithmic HBM bytes of one decode step (K and V of every visible token, q in, out)."""
         g = self.wl.geom
         esz = 2 if g.dtype == "bf16" else 4
-        toks = sum(sum(s.length for s in self.ctx_segs[r]) + int(self.pre_len[r]) + step + 1 for r in range(self.R))
+        toks = int(np.sum(self._ctx_tokens + self.pre_len)) + self.R * (step + 1)
         return toks * 2 * g.num_kv_heads * g.head_dim * esz + 2 * self.R * g.num_q_heads * g.head_dim * esz

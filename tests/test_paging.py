@@ -93,3 +93,32 @@ def test_order_for_reuse_lists_shared_documents_first_and_keeps_everything():
         assert sorted(map(key, before.segments)) == sorted(map(key, after.segments))
         assert not after.segments[-1].ctx or all(sg.ctx for sg in after.segments)
         assert after.length == before.length
+
+
+def test_unpinned_count_tracks_every_transition():
+    """room_for_private relies on a running count of unpinned blocks: it must equal the plain sum after any
+    mix of hits, misses, releases, forgets and evictions."""
+    import numpy as np
+
+    from position_agnostic_paged_amd.paging import BlockPool, DocCache
+
+    rng = np.random.default_rng(0)
+    cache = DocCache(BlockPool(200), budget_blocks=150)
+    held = []
+    for _ in range(2000):
+        op = rng.integers(0, 4)
+        if op < 2:
+            d = int(rng.integers(0, 40))
+            try:
+                cache.acquire(d, int(16 * (1 + d % 5)))
+                held.append(d)
+            except Exception:
+                pass
+        elif op == 2 and held:
+            cache.release(held.pop(int(rng.integers(0, len(held)))))
+        elif op == 3 and len(cache):
+            d = next(iter(cache._docs))
+            if d not in held:
+                cache.forget(d)
+        want = sum(len(x.blocks) for x in cache._docs.values() if x.pins == 0)
+        assert cache.unpinned == want
