@@ -257,13 +257,12 @@ lazy_status lazy_attn_decode(const lazy_geom* geom, const lazy_pos_desc* pos, co
  * keeps a tile list of its unshared documents and private tokens (same
  * layout as lazy_build_tiles).  Work items: (document, first 16-row block,
  * chunk, tiles per chunk) covering reads x (num_q_heads / num_kv_heads) rows
- * per document, row_blocks x 16 rows each, and the document's tiles in
- * chunks (one per document unless the pass would hold fewer than 1024
- * waves; then up to ceil(2048 / waves) even chunks of >= 32 tiles); a read
+ * per document, row_blocks x 16 rows each (row_blocks: 8 for bf16, one
+ * workgroup of the LDS-staged pass; for fp32 one wave, 2 at dh 128, 4 at
+ * dh 64), and the document's tiles in chunks (one per document unless the
+ * pass would hold fewer than F work items, F = 256 for bf16 and 1024 for
+ * fp32; then up to ceil(2 F / items) even chunks of >= 32 tiles); a read
  * takes one partial slot per chunk of its document, from its slot field on.
- * (A build with workgroups of several doc-pass waves pads each (document,
- * chunk)'s items to a multiple of that count with empty items, first row
- * block past the document's rows.)
  * Outputs (caller-allocated): tiles_out[tiles_cap], tile_start[R+1],
  * ctx_tiles[R]; doc_tiles_out[doc_tiles_cap]; doc_tile_start, read_start
  * [docs_cap+1]; reads_out[reads_cap]; req_reads[R] (shared-read slots per

@@ -168,13 +168,12 @@ __global__ __launch_bounds__(64 * WT) __attribute__((amdgpu_waves_per_eu(WPE))) 
 // head per XCD, and a document's row blocks are adjacent work items, so the
 // waves reading one document's head slice share an L2.
 template <typename T, int DH, int KIND, int RB, int WPE>
-__global__ __launch_bounds__(64 * kDocPassWgWaves) __attribute__((amdgpu_waves_per_eu(WPE))) void docpass_kernel(
-    AttnArgs a, DocPassArgs d) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WPE))) void docpass_kernel(AttnArgs a,
+                                                                                               DocPassArgs d) {
   using W = WaveAttn<T, DH, KIND, false, false, RB>;
   const int lane = threadIdx.x & 63;
   const int kvh = blockIdx.x;
-  // the workgroup's waves are the row blocks of one (document, chunk)
-  const int item = blockIdx.y * kDocPassWgWaves + (threadIdx.x >> 6);
+  const int item = blockIdx.y;
   const int doc = d.work[4 * item];
   const int rb0 = d.work[4 * item + 1];
   const int chunk = d.work[4 * item + 2];
@@ -483,14 +482,12 @@ hipError_t launch_combine(const AttnArgs& a, const Plan& p, const int32_t* q_sta
 // The document pass for one (dtype, head_dim, kind).
 template <typename T, int DH, int KIND>
 hipError_t launch_docpass(const AttnArgs& a, const DocPassArgs& d, int rb, int num_work, int hkv, hipStream_t st) {
-  if (num_work % kDocPassWgWaves != 0) return hipErrorInvalidValue;  // the plan pads every group
-  dim3 grid((unsigned)hkv, (unsigned)(num_work / kDocPassWgWaves));
+  dim3 grid((unsigned)hkv, (unsigned)num_work);
   // the row blocks docpass_row_blocks gives: 2 at dh 128, 4 at dh 64 (both
   // within two waves per SIMD)
   constexpr int RB = (DH == 128) ? LAZY_DOCPASS_RB128 : 4;
   if (rb != RB) return hipErrorNotSupported;
-  hipLaunchKernelGGL((docpass_kernel<T, DH, KIND, RB, LAZY_DOCPASS_WPE>), grid, dim3(64 * kDocPassWgWaves), 0, st,
-                     a, d);
+  hipLaunchKernelGGL((docpass_kernel<T, DH, KIND, RB, LAZY_DOCPASS_WPE>), grid, dim3(64), 0, st, a, d);
   return hipGetLastError();
 }
 
@@ -769,7 +766,10 @@ hipError_t run_shared(const lazy_pos_desc* pd, const AttnArgs& a, const DocPassA
     AttnArgs ad = a;
     ad.tiles = d.doc_tiles;
     ad.tile_start = d.doc_tile_start;
-    e = docpass_kind<T, DH>(pd->kind, ad, d, rb, num_work, hkv, st);
+    if constexpr (std::is_same<T, bf16>::value && LAZY_DOCPASS_LDS)
+      e = launch_docpass_lds(ad, d, pd->kind, DH, num_work, hkv, st);
+    else
+      e = docpass_kind<T, DH>(pd->kind, ad, d, rb, num_work, hkv, st);
     if (e != hipSuccess) return e;
   }
   // 3. per (request, head): the request's split partials and its reads' partials
@@ -802,12 +802,9 @@ extern "C" lazy_status lazy_attn_decode_shared(
   if (num_docs < 0 || num_work < 0 || max_req_reads < 0 || max_req_reads > 65536)
     return fail(LAZY_ERR_ARG, "num_docs, num_work >= 0 and max_req_reads in [0, 65536] required");
   if (row_blocks != docpass_row_blocks(geom))
-    return fail(LAZY_ERR_ARG, "the plan was built for %d row blocks per wave; this geometry runs %d", row_blocks,
+    return fail(LAZY_ERR_ARG, "the plan was built for %d row blocks per work item; this geometry runs %d", row_blocks,
                 docpass_row_blocks(geom));
-  if (num_work / kDocPassWgWaves > 65535) return fail(LAZY_ERR_UNSUPPORTED, "too many document work items");
-  if (num_work % kDocPassWgWaves != 0)
-    return fail(LAZY_ERR_ARG, "num_work %d is not a multiple of %d (the plan pads each document's items)", num_work,
-                kDocPassWgWaves);
+  if (num_work > 65535) return fail(LAZY_ERR_UNSUPPORTED, "too many document work items (%d > 65535)", num_work);
   if (num_work > 0 && (!doc_tiles || !doc_tile_start || !read_start || !reads || !work))
     return fail(LAZY_ERR_ARG, "a document-pass array is NULL");
   if (num_reqs > 0 && !req_reads) return fail(LAZY_ERR_ARG, "req_reads is NULL");

@@ -611,4 +611,9 @@ __device__ __forceinline__ bool split_range(int nt, int chunk, int max_splits, i
 hipError_t launch_prefill_lds(const AttnArgs& a, int kind, bool defer, int head_dim, int rb, int row_tiles,
                               int splits, int num_reqs, int hkv, hipStream_t st);
 
+// Launches the LDS-staged document pass (bf16; prefill_lds.hip): grid (KV
+// head, work item), each item docpass_row_blocks x 16 rows.
+hipError_t launch_docpass_lds(const AttnArgs& a, const DocPassArgs& d, int kind, int head_dim, int num_work, int hkv,
+                              hipStream_t st);
+
 }  // namespace lazy

@@ -340,18 +340,20 @@ extern "C" lazy_status lazy_build_shared_plan(
   doc_tile_start[docs.size()] = (int32_t)ndt;
 
   // 4. chunks: a document pass of few, long documents would leave most of
-  //    the chip idle.  When the pass holds fewer than kFewWaves waves (half
-  //    a resident round), each document is cut into up to ceil(kDocPassWaves
-  //    / waves) even chunks of >= kMinChunkTiles tiles, a chunk per wave and
-  //    its own partial slot per read; otherwise documents stay whole (every
-  //    chunk adds a partial per read and per head to merge)
+  //    the chip idle.  When the pass holds fewer than `few` work items (half
+  //    a resident round: 256 workgroups of the LDS pass, one per CU, or 1024
+  //    waves of the per-wave pass), each document is cut into up to
+  //    ceil(2 few / items) even chunks of >= kMinChunkTiles tiles, a chunk
+  //    per item and its own partial slot per read; otherwise documents stay
+  //    whole (every chunk adds a partial per read and per head to merge)
   const int32_t group = geom->num_q_heads / geom->num_kv_heads;
   const int32_t rb = docpass_row_blocks(geom);
-  constexpr int64_t kFewWaves = 1024, kDocPassWaves = 2048, kMinChunkTiles = 32;
-  int64_t waves = 0;
-  for (const Doc& d : docs) waves += ((int64_t)d.readers * group + 16 * rb - 1) / (16 * rb);
-  waves *= geom->num_kv_heads;
-  const int64_t want_chunks = (waves > 0 && waves < kFewWaves) ? (kDocPassWaves + waves - 1) / waves : 1;
+  const int64_t few = docpass_uses_lds(geom) ? 256 : 1024;
+  constexpr int64_t kMinChunkTiles = 32;
+  int64_t items = 0;
+  for (const Doc& d : docs) items += ((int64_t)d.readers * group + 16 * rb - 1) / (16 * rb);
+  items *= geom->num_kv_heads;
+  const int64_t want_chunks = (items > 0 && items < few) ? (2 * few + items - 1) / items : 1;
   std::vector<int32_t> nchunks(docs.size()), chunk_tiles(docs.size());
   for (size_t i = 0; i < docs.size(); ++i) {
     const int64_t nt_doc = (seg_len[docs[i].first_seg] + LAZY_BLOCK_SIZE - 1) / LAZY_BLOCK_SIZE;
@@ -427,20 +429,17 @@ extern "C" lazy_status lazy_build_shared_plan(
 
   // 6. work items of the document pass: (document, first 16-row block,
   //    chunk, tiles per chunk) for every docpass_row_blocks x 16 rows of
-  //    reads x query group and every chunk; a document's items adjacent
-  //    Each (document, chunk)'s items are padded to a multiple of
-  //    kDocPassWgWaves with empty items (first row block past the rows) so
-  //    that a workgroup holds one document's row blocks only.
+  //    reads x query group and every chunk; a (document, chunk)'s row tiles
+  //    adjacent
   int64_t nw = 0;
   for (size_t i = 0; i < docs.size(); ++i) {
     const int64_t rows = (int64_t)docs[i].readers * group;
-    const int64_t items = (rows + 16 * rb - 1) / (16 * rb);
-    const int64_t padded = (items + kDocPassWgWaves - 1) / kDocPassWgWaves * kDocPassWgWaves;
+    const int64_t n_items = (rows + 16 * rb - 1) / (16 * rb);
     for (int32_t c = 0; c < nchunks[i]; ++c)
-      for (int64_t k = 0; k < padded; ++k) {
+      for (int64_t k = 0; k < n_items; ++k) {
         if (nw >= work_cap) return fail(LAZY_ERR_ARG, "work_cap %lld too small", (long long)work_cap);
         work_out[4 * nw] = (int32_t)i;
-        work_out[4 * nw + 1] = (int32_t)(k < items ? k * rb : (rows + 15) / 16);  // empty: no rows left
+        work_out[4 * nw + 1] = (int32_t)(k * rb);
         work_out[4 * nw + 2] = c;
         work_out[4 * nw + 3] = chunk_tiles[i];
         ++nw;

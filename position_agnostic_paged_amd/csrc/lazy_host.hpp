@@ -18,22 +18,31 @@ lazy_status check_geom(const lazy_geom* g);
 // Positional-descriptor checks (needs_rotation: the call reads cos/sin).
 lazy_status check_pos(const lazy_geom* g, const lazy_pos_desc* p);
 
-// 16-row blocks per wave of the document-major decode pass (rows = reads of
-// one shared document x the query group); the planner and the launch agree
-// through this one function.
+// The document pass of the document-major decode (rows = reads of one shared
+// document x the query group).  bf16 runs the LDS-staged pass: a workgroup of
+// kDocPassLdsWaves waves, kDocPassLdsRb blocks of 16 rows each, copies each
+// tile pair once for all its rows.  fp32 runs the per-wave pass,
+// LAZY_DOCPASS_RB128 (dh 128) or 4 (dh 64) row blocks per wave.
 #ifndef LAZY_DOCPASS_RB128
 #define LAZY_DOCPASS_RB128 2
 #endif
-inline int docpass_row_blocks(const lazy_geom* g) { return g->head_dim == 128 ? LAZY_DOCPASS_RB128 : 4; }
-// Waves per workgroup of the document pass.  Above 1, the row-block waves of
-// one (document, chunk) are grouped in workgroups of this many (the planner
-// pads each group with empty items), so they run on one CU and read the same
-// tiles at about the same time; measured slower on MI355X (mixed 70B step
-// decode 0.36 ms at 1, 0.50 / 0.57 / 0.51 ms at 2 / 4 / 8: padding and
-// whole-workgroup residency cost more than the shared reads gain).
-#ifndef LAZY_DOCPASS_WG_WAVES
-#define LAZY_DOCPASS_WG_WAVES 1
+#ifndef LAZY_DOCPASS_LDS_WAVES
+#define LAZY_DOCPASS_LDS_WAVES 4
 #endif
-constexpr int kDocPassWgWaves = LAZY_DOCPASS_WG_WAVES;
+#ifndef LAZY_DOCPASS_LDS_RB
+#define LAZY_DOCPASS_LDS_RB 2
+#endif
+constexpr int kDocPassLdsWaves = LAZY_DOCPASS_LDS_WAVES;
+constexpr int kDocPassLdsRb = LAZY_DOCPASS_LDS_RB;
+#ifndef LAZY_DOCPASS_LDS
+#define LAZY_DOCPASS_LDS 1  // 0: bf16 runs the per-wave pass too
+#endif
+inline bool docpass_uses_lds(const lazy_geom* g) { return LAZY_DOCPASS_LDS && g->dtype == LAZY_BF16; }
+// 16-row blocks of one work item (a workgroup of the LDS pass, a wave of the
+// per-wave pass); the planner and the launch agree through this one function.
+inline int docpass_row_blocks(const lazy_geom* g) {
+  if (docpass_uses_lds(g)) return kDocPassLdsWaves * kDocPassLdsRb;
+  return g->head_dim == 128 ? LAZY_DOCPASS_RB128 : 4;
+}
 
 }  // namespace lazy

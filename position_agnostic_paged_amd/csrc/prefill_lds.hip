@@ -48,6 +48,16 @@ namespace lazy {
                               // 4 x 16 rows: spills at dh 128, the rescale keeps the accumulators in VGPRs)
 #endif
 constexpr int kPrefillWaves = LAZY_PREFILL_WAVES;
+// The document pass's ring: LAZY_DOCPASS_STAGES tile pairs (four: 64 KiB at
+// dh 128, so two workgroups share a CU and one's ring fill and barriers
+// overlap the other's work), and a register cap for LAZY_DOCPASS_LDS_WPE
+// waves per SIMD (both workgroups resident).
+#ifndef LAZY_DOCPASS_STAGES
+#define LAZY_DOCPASS_STAGES 4
+#endif
+#ifndef LAZY_DOCPASS_LDS_WPE
+#define LAZY_DOCPASS_LDS_WPE (LAZY_DOCPASS_LDS_WAVES / 2)
+#endif
 constexpr int kLdsBytes = 160 * 1024;    // LDS of one CU, all of it for the ring
 
 // Wait until at most N vector-memory operations of this wave are outstanding
@@ -80,7 +90,7 @@ __device__ __forceinline__ void wait_stages(int n) {
   }
 }
 
-template <int DH, bool ROT, int NW>
+template <int DH, bool ROT, int NW, int MAXS = 10>
 struct StageGeom {
   static constexpr int kTile = kBlock * DH * 2;      // bytes of one 16 x dh bf16 tile
   static constexpr int kChunksPerRow = DH / 8;       // 16-byte chunks in a K row
@@ -92,11 +102,17 @@ struct StageGeom {
   static constexpr int kKChunks = 2 * kTile / 16;    // 16-B chunks of the K pair (same for V)
   static constexpr int kCopies = 2 * kKChunks / (NW * 64);  // K + V copies per thread
   static constexpr int kLoads = kCopies + (ROT ? 1 : 0);    // copies per wave per stage
-  static constexpr int kStages = (kLdsBytes / kBytes) < 10 ? (kLdsBytes / kBytes) : 10;
+  static constexpr int kStages = (kLdsBytes / kBytes) < MAXS ? (kLdsBytes / kBytes) : MAXS;
+  static constexpr int kLdsTotal = kStages * kBytes;
+  // Pairs past the consumed one that each iteration waits for: with the K
+  // rotation, pair p + 2 (rotated during iteration p); without it, pair
+  // p + 1 (its scores end iteration p), which leaves one more stage in flight
+  // and lets a ring of four stages work.
+  static constexpr int kAhead = ROT ? 2 : 1;
   // every wave issues the same number of copies (the counted waits rely on
   // it) and no wave's 64 chunks straddle the K / V boundary
   static_assert(kCopies >= 1 && (2 * kKChunks) % (NW * 64) == 0 && kKChunks % 64 == 0, "stage copy shape");
-  static_assert(kStages >= 5 && (kStages - 3) * kLoads < 64, "ring depth");
+  static_assert(kStages >= 3 + kAhead && (kStages - 1 - kAhead) * kLoads < 64, "ring depth");
   // rotation items: 16 rows x dh/8 items (4 rotation pairs each) per tile
   static constexpr int kRotItems = kBlock * DH / 8;
   static_assert(kRotItems % 64 == 0, "rotation items per wave");
@@ -157,14 +173,14 @@ __device__ __forceinline__ void xcd_unit(int wg, int num_wgs, int splits, int hk
   row_tile = t;
 }
 
-template <int DH, int KIND, bool DEFER, int RB, int NW>
+template <int DH, int KIND, bool DEFER, int RB, int NW, int MAXS = 10>
 struct LdsPrefill {
   using F8 = bf16x8;
   using F4 = bf16x4;
   static constexpr int NC = DH / 32;  // contraction chunks of QK^T
   static constexpr int NV = DH / 16;  // 16-channel blocks of the output
   static constexpr bool kRot = (KIND != kAlibi) && DEFER;
-  using SG = StageGeom<DH, kRot, NW>;
+  using SG = StageGeom<DH, kRot, NW, MAXS>;
   static constexpr int S = SG::kStages;
 
   const AttnArgs& a;
@@ -401,67 +417,31 @@ struct LdsPrefill {
   }
 };
 
-template <int DH, int KIND, bool DEFER, int RB, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int row_tiles, int num_wgs) {
-  using P = LdsPrefill<DH, KIND, DEFER, RB, NW>;
+// The pipelined loop over a unit's tile pairs, shared by the prefill and the
+// document pass: every wave of the workgroup copies (and, with deferred
+// rotation, rotates) the pairs; a wave with rows (has_rows) also runs its RB
+// blocks of 16 query rows qr against them.  Returns the wave's unnormalised
+// accumulators, row sums (replicated in the four registers) and log2-domain
+// reference maxima.  qp is each row's query position and slope_raw its ALiBi
+// slope over the softmax scale (masking: causal against private tiles, the
+// bias against every tile).
+template <int DH, int KIND, bool DEFER, int RB, int NW, int MAXS>
+__device__ __forceinline__ void lds_attend(LdsPrefill<DH, KIND, DEFER, RB, NW, MAXS>& pl,
+                                           const typename LdsPrefill<DH, KIND, DEFER, RB, NW, MAXS>::F8 (&qr)[RB][DH / 32],
+                                           const int (&qp)[RB], const float (&slope_raw)[RB], bool has_rows,
+                                           f32x4 (&acc)[RB][DH / 16], f32x4 (&lsum)[RB], float (&m_run)[RB]) {
+  using P = LdsPrefill<DH, KIND, DEFER, RB, NW, MAXS>;
   using F8 = typename P::F8;
-  using F4 = typename P::F4;
   constexpr int NC = P::NC;
   constexpr int NV = P::NV;
   using SG = typename P::SG;
   constexpr int S = P::S;
-  extern __shared__ __align__(16) unsigned char lds_buf[];
-
-  // ids through the intrinsics (no library call: a call's results would
-  // not be known to be wave-uniform)
-  const int tid = __builtin_amdgcn_workitem_id_x();
-  const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
+  const AttnArgs& a = pl.a;
+  // ids through the intrinsics again (measured: fewer registers than the copies in pl)
+  const int lane = __builtin_amdgcn_workitem_id_x() & 63;
+  const int wave = uniform((int)__builtin_amdgcn_workitem_id_x() >> 6);
+  const int npairs = pl.npairs;
   const int r = lane & 15, g = lane >> 4;
-  int req, kvh, split, row_tile;
-  xcd_unit(__builtin_amdgcn_workgroup_id_x(), num_wgs, a.num_splits, a.hkv, row_tiles, req, kvh, split, row_tile);
-
-  const int q0 = a.q_start[req];
-  int nq = a.q_start[req + 1] - q0;
-  nq = min(nq, a.max_q_len);
-  nq = max(0, min(nq, a.rows_bound / a.hq - q0));
-  const int nrows = nq * a.group;
-  const int t0 = a.tile_start[req];
-  const int nt = a.tile_start[req + 1] - t0;
-  int sb, se;
-  // workgroup-uniform exits only (barriers follow)
-  if (row_tile * NW * RB * 16 >= nrows) return;
-  if (!split_range(nt, a.chunk, a.num_splits, split, sb, se)) return;
-  const int npairs = (se - sb + 1) >> 1;
-  const int rb0 = (row_tile * NW + wave) * RB;
-  const bool has_rows = rb0 * 16 < nrows;  // wave-uniform: waves without rows still copy and rotate
-  const int qpos0 = a.q_pos[req];
-
-  P pl{a, lds_buf, tid, lane, wave, kvh, sb, se, a.ctx_tiles[req], npairs, (const_words)(a.tiles + t0), {}};
-  pl.init_copies();
-
-  // Query rows at their global positions: row rho of the request is
-  // (token rho / G, head kvh*G + rho % G); rows past the request's last are
-  // zero (computed, never stored).
-  int qp[RB];
-  float slope_raw[RB];
-  F8 qr[RB][NC];
-#pragma unroll
-  for (int b = 0; b < RB; ++b) {
-    const int rho = (rb0 + b) * 16 + r;
-    const bool ok = rho < nrows;
-    const int qi = ok ? rho / a.group : 0;
-    const int head = kvh * a.group + (ok ? rho % a.group : 0);
-    qp[b] = qpos0 + qi;
-    // ALiBi in the raw-score domain: bias / softmax scale
-    slope_raw[b] = (KIND == kAlibi) ? a.slopes[head] * kLog2e / a.scale_log2 : 0.f;
-    const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + ((int64_t)(q0 + qi) * a.hq + head) * DH;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const F8 v = *reinterpret_cast<const F8*>(qrow + 32 * c + 8 * g);
-      qr[b][c] = ok ? v : F8{};
-    }
-  }
 
   // Fragment offsets inside a stage (loop-invariant).  K product h, chunk c:
   // row r of the product is key (tile r/8, token 8 ((r/4)%2) + 4h + r%4), so
@@ -479,9 +459,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
   }
   const uint32_t voff = SG::kV + (g >> 1) * SG::kTile + r * 32 + (((g & 1) ^ ((r >> 3) & 1)) << 4);
 
-  f32x4 acc[RB][NV];
-  f32x4 lsum[RB];  // row sums, replicated in the four registers
-  float m_run[RB], negm[RB], thr[RB];
+  float negm[RB], thr[RB];
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
 #pragma unroll
@@ -496,27 +474,30 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
 #pragma unroll
   for (int t = 0; t < 8; ++t) ones[t] = (bf16)1.f;
 
-  // prologue: S - 1 pairs in flight; pairs 0 and 1 landed and rotated;
-  // scores of pair 0
+  // prologue: S - 1 pairs in flight; pairs 0 .. kA - 1 landed (and, with
+  // the K rotation, rotated); scores of pair 0
+  constexpr int kA = SG::kAhead;
 #pragma unroll
   for (int q = 0; q < S - 1; ++q)
     if (q < npairs) pl.issue(q, pl.load_words(q));
-  wait_stages<SG::kLoads, S - 3>(min(S - 3, npairs - 2));
+  wait_stages<SG::kLoads, S - 1 - kA>(min(S - 1 - kA, npairs - kA));
   asm volatile("s_barrier" ::: "memory");
   // Tile words of the pair to copy next travel through scalar registers, read
   // one iteration ahead; the later stages use the pair's decoded header,
   // likewise read one iteration ahead (pair p + 1 for the softmax, p + 3 for
   // the rotation).
   PairWords wi = pl.load_words(S - 1);
-  pl.rotate_stage(0);
-  if (1 < npairs) pl.rotate_stage(1);
   u32x4 hc;
-  int dr[2];
+  int dr[2] = {0, 0};
   {
     const u32x4 h = pl.read_hdr(0);
-    const u32x2 d = pl.read_deltas(2);
 #pragma unroll
     for (int k = 0; k < 4; ++k) hc[k] = (uint32_t)uniform((int)h[k]);
+  }
+  if constexpr (P::kRot) {
+    pl.rotate_stage(0);
+    if (1 < npairs) pl.rotate_stage(1);
+    const u32x2 d = pl.read_deltas(2);
     dr[0] = uniform((int)d[0]);
     dr[1] = uniform((int)d[1]);
   }
@@ -530,18 +511,19 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
     asm volatile("" : "+s"(sp));  // one opaque scalar (see stage_off)
     pl.base_q = p;
     pl.base_off = sp;
-    // Own copies of pair p + 2 complete: at most the later pairs' copies
-    // (p + 3 .. p + S - 2) stay outstanding.
-    wait_stages<SG::kLoads, S - 4>(max(0, min(S - 4, npairs - 3 - p)));
-    // The barrier makes pair p + 2 complete for all waves, publishes the
+    // Own copies of pair p + kA complete: at most the later pairs' copies
+    // (p + kA + 1 .. p + S - 2) stay outstanding.
+    wait_stages<SG::kLoads, S - 2 - kA>(max(0, min(S - 2 - kA, npairs - 1 - kA - p)));
+    // The barrier makes pair p + kA complete for all waves, publishes the
     // rotation of pair p + 1, and frees buffer (p - 1) % S (its V was read
     // at iteration p - 1, its K at p - 2).  A bare s_barrier (compiler
     // memory clobber only): a fenced __syncthreads would also drain the
     // copies of the later pairs still in flight.
     asm volatile("s_barrier" ::: "memory");
-    // headers for the next iteration (written at least three barriers ago)
+    // headers for the next iteration (written at least two barriers ago)
     const u32x4 hv_next = pl.read_hdr(p + 1);
-    const u32x2 dv_next = pl.read_deltas(p + 3);
+    u32x2 dv_next = {0u, 0u};
+    if constexpr (P::kRot) dv_next = pl.read_deltas(p + 3);
     // Rotation of pair p + 2 in two halves: its LDS reads now, its
     // arithmetic and write-back (with the next copies) in the other half of
     // the iteration from this pair's softmax and products.
@@ -664,6 +646,72 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
     dr[1] = uniform((int)dv_next[1]);
     sp = pl.stage_off(p + 1);
   }
+}
+
+template <int DH, int KIND, bool DEFER, int RB, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int row_tiles, int num_wgs) {
+  using P = LdsPrefill<DH, KIND, DEFER, RB, NW>;
+  using F8 = typename P::F8;
+  using F4 = typename P::F4;
+  constexpr int NC = P::NC;
+  constexpr int NV = P::NV;
+  extern __shared__ __align__(16) unsigned char lds_buf[];
+
+  // ids through the intrinsics (no library call: a call's results would
+  // not be known to be wave-uniform)
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  int req, kvh, split, row_tile;
+  xcd_unit(__builtin_amdgcn_workgroup_id_x(), num_wgs, a.num_splits, a.hkv, row_tiles, req, kvh, split, row_tile);
+
+  const int q0 = a.q_start[req];
+  int nq = a.q_start[req + 1] - q0;
+  nq = min(nq, a.max_q_len);
+  nq = max(0, min(nq, a.rows_bound / a.hq - q0));
+  const int nrows = nq * a.group;
+  const int t0 = a.tile_start[req];
+  const int nt = a.tile_start[req + 1] - t0;
+  int sb, se;
+  // workgroup-uniform exits only (barriers follow)
+  if (row_tile * NW * RB * 16 >= nrows) return;
+  if (!split_range(nt, a.chunk, a.num_splits, split, sb, se)) return;
+  const int npairs = (se - sb + 1) >> 1;
+  const int rb0 = (row_tile * NW + wave) * RB;
+  const bool has_rows = rb0 * 16 < nrows;  // wave-uniform: waves without rows still copy and rotate
+  const int qpos0 = a.q_pos[req];
+
+  P pl{a, lds_buf, tid, lane, wave, kvh, sb, se, a.ctx_tiles[req], npairs, (const_words)(a.tiles + t0), {}};
+  pl.init_copies();
+
+  // Query rows at their global positions: row rho of the request is
+  // (token rho / G, head kvh*G + rho % G); rows past the request's last are
+  // zero (computed, never stored).
+  int qp[RB];
+  float slope_raw[RB];
+  F8 qr[RB][NC];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int rho = (rb0 + b) * 16 + r;
+    const bool ok = rho < nrows;
+    const int qi = ok ? rho / a.group : 0;
+    const int head = kvh * a.group + (ok ? rho % a.group : 0);
+    qp[b] = qpos0 + qi;
+    // ALiBi in the raw-score domain: bias / softmax scale
+    slope_raw[b] = (KIND == kAlibi) ? a.slopes[head] * kLog2e / a.scale_log2 : 0.f;
+    const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + ((int64_t)(q0 + qi) * a.hq + head) * DH;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const F8 v = *reinterpret_cast<const F8*>(qrow + 32 * c + 8 * g);
+      qr[b][c] = ok ? v : F8{};
+    }
+  }
+
+  f32x4 acc[RB][NV];
+  f32x4 lsum[RB];
+  float m_run[RB];
+  lds_attend<DH, KIND, DEFER, RB, NW, 10>(pl, qr, qp, slope_raw, has_rows, acc, lsum, m_run);
   if (!has_rows) return;
 
   // O[row r][16n + 4g + j] = acc[b][n][j]: normalised output (one split) or an
@@ -697,28 +745,149 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
   }
 }
 
+// The document pass of the document-major decode on the same ring: one
+// workgroup per (work item, KV head), a work item being up to NW x RB x 16
+// rows (reads of one shared document x the query group) against one chunk of
+// the document's tiles.  The tiles are copied once per workgroup for all
+// those rows; each row's query is rotated by -Delta of its read on the way
+// into registers (the single relative rotation, LazyAttention notes,
+// "Key designs": decode rotates the query) and the keys stay at their local
+// positions, so the ring runs without its K rotation.  Every row ends as an
+// (m, l, acc) partial in its read's slot (one per chunk), which the decode
+// combine merges with the request's other partials.  Grid (KV head, work
+// item): with eight KV heads a head is one XCD, and a document's row tiles
+// are adjacent items there, so the second one finds the tiles in L2.
+template <int DH, int KIND, int RB, int NW, int MAXS, int WPE>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) void docpass_lds_kernel(
+    AttnArgs a, DocPassArgs d) {
+  using P = LdsPrefill<DH, KIND, false, RB, NW, MAXS>;
+  using F8 = typename P::F8;
+  constexpr int NC = P::NC;
+  constexpr int NV = P::NV;
+  extern __shared__ __align__(16) unsigned char lds_buf[];
+
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int kvh = __builtin_amdgcn_workgroup_id_x();
+  const int item = __builtin_amdgcn_workgroup_id_y();
+  const int doc = d.work[4 * item];
+  const int b0 = d.work[4 * item + 1];
+  const int chunk = d.work[4 * item + 2];
+  const int ct = d.work[4 * item + 3];
+  const int dt0 = d.doc_tile_start[doc];
+  const int nt_doc = d.doc_tile_start[doc + 1] - dt0;
+  const int tb = min(nt_doc, chunk * ct);
+  const int nt = min(nt_doc - tb, ct);
+  const int read0 = d.read_start[doc];
+  const int nrows = (d.read_start[doc + 1] - read0) * a.group;
+  // workgroup-uniform exits only (barriers follow)
+  if (b0 * 16 >= nrows || nt <= 0) return;
+  const int npairs = (nt + 1) >> 1;
+  const int rb0 = b0 + wave * RB;
+  const bool has_rows = rb0 * 16 < nrows;
+
+  // every tile of the chunk is a context tile at its local position
+  P pl{a, lds_buf, tid, lane, wave, kvh, 0, nt, nt, npairs, (const_words)(d.doc_tiles + dt0 + tb), {}};
+  pl.init_copies();
+
+  // Row rho = (read rho / G, head kvh*G + rho % G): that request's query
+  // rotated by -Delta; ALiBi measures the distance from q_pos - Delta, the
+  // keys sitting at Delta + their local positions.  A Delta the table cannot
+  // serve is never looked up: its rows' partials are stored as NaN bit
+  // patterns (this file is built without NaN semantics, so no NaN value is
+  // ever computed here).
+  int qp[RB], delta[RB];
+  float slope_raw[RB];
+  int64_t prow[RB];
+  bool bad[RB];
+  const bf16* qptr[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int rho = (rb0 + b) * 16 + r;
+    const int rr = rho < nrows ? rho : 0;
+    int req, slot, dl;
+    unpack_read(d.reads[read0 + rr / a.group], req, slot, dl);
+    const int head = kvh * a.group + rr % a.group;
+    qptr[b] = reinterpret_cast<const bf16*>(a.q) + ((int64_t)req * a.hq + head) * DH;
+    qp[b] = a.q_pos[req] - dl;
+    slope_raw[b] = (KIND == kAlibi) ? a.slopes[head] * kLog2e / a.scale_log2 : 0.f;
+    prow[b] = (int64_t)(d.slot_base + slot + chunk) * a.rows_bound + ((int64_t)req * a.hq + head);
+    bad[b] = KIND != kAlibi && a.cos_sin != nullptr && (dl < 0 || dl >= a.max_pos);
+    delta[b] = (KIND == kAlibi || bad[b]) ? 0 : dl;
+  }
+  F8 qr[RB][NC];
+  const int active = has_rows ? min(RB, (nrows - rb0 * 16 + 15) / 16) : 0;
+  rotate_query_rows<bf16, DH, KIND, RB>(qr, qptr, a, delta, g, active);
+
+  f32x4 acc[RB][NV];
+  f32x4 lsum[RB];
+  float m_run[RB];
+  lds_attend<DH, KIND, false, RB, NW, MAXS>(pl, qr, qp, slope_raw, has_rows, acc, lsum, m_run);
+  if (!has_rows) return;
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    if ((rb0 + b) * 16 + r >= nrows) continue;
+    float* po = a.part_o + prow[b] * DH + 4 * g;
+    if (bad[b]) {
+      constexpr uint32_t kQNaN = 0x7FC00000u;
+      const u32x4 nan4 = {kQNaN, kQNaN, kQNaN, kQNaN};
+#pragma unroll
+      for (int n = 0; n < NV; ++n) *reinterpret_cast<u32x4*>(po + 16 * n) = nan4;
+      if (g == 0) {
+        const u32x2 nan2 = {kQNaN, kQNaN};
+        *reinterpret_cast<u32x2*>(a.part_ml + prow[b] * 2) = nan2;
+      }
+      continue;
+    }
+#pragma unroll
+    for (int n = 0; n < NV; ++n) *reinterpret_cast<f32x4*>(po + 16 * n) = acc[b][n];
+    if (g == 0) {
+      a.part_ml[prow[b] * 2 + 0] = m_run[b];
+      a.part_ml[prow[b] * 2 + 1] = lsum[b][0];
+    }
+  }
+}
+
 namespace {
 
-template <int DH, int KIND, bool DEFER, int RB>
-hipError_t launch_rb(const AttnArgs& a, int row_tiles, int splits, int num_reqs, int hkv, hipStream_t st) {
-  constexpr int NW = kPrefillWaves;
-  constexpr bool rot = (KIND != kAlibi) && DEFER;
-  using SG = StageGeom<DH, rot, NW>;
-  const size_t lds = (size_t)SG::kStages * SG::kBytes;
-  // The ring needs more than the default 64 KiB of dynamic LDS: the attribute
-  // is set once per device (a second setting is harmless, so racing threads
-  // need no lock).
+// The ring needs more than the default 64 KiB of dynamic LDS: the attribute
+// is set once per device and kernel (a second setting is harmless, so racing
+// threads need no lock).
+template <const void* (*KERNEL)()>
+hipError_t ensure_lds_attr(size_t lds) {
   static std::atomic<uint64_t> attr_set{0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
   if (bit == 0 || !(attr_set.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_lds_kernel<DH, KIND, DEFER, RB, NW>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    e = hipFuncSetAttribute(KERNEL(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_release);
   }
+  return hipSuccess;
+}
+
+template <int DH, int KIND, bool DEFER, int RB, int NW>
+const void* prefill_kernel_ptr() {
+  return reinterpret_cast<const void*>(&prefill_lds_kernel<DH, KIND, DEFER, RB, NW>);
+}
+
+template <int DH, int KIND, int RB, int NW, int MAXS, int WPE>
+const void* docpass_kernel_ptr() {
+  return reinterpret_cast<const void*>(&docpass_lds_kernel<DH, KIND, RB, NW, MAXS, WPE>);
+}
+
+template <int DH, int KIND, bool DEFER, int RB>
+hipError_t launch_rb(const AttnArgs& a, int row_tiles, int splits, int num_reqs, int hkv, hipStream_t st) {
+  constexpr int NW = kPrefillWaves;
+  constexpr bool rot = (KIND != kAlibi) && DEFER;
+  using SG = StageGeom<DH, rot, NW>;
+  const size_t lds = (size_t)SG::kLdsTotal;
+  hipError_t e = ensure_lds_attr<prefill_kernel_ptr<DH, KIND, DEFER, RB, NW>>(lds);
+  if (e != hipSuccess) return e;
   const int num_wgs = row_tiles * splits * hkv * num_reqs;  // 1-D: the kernel maps ids to units
   hipLaunchKernelGGL((prefill_lds_kernel<DH, KIND, DEFER, RB, NW>), dim3((unsigned)num_wgs), dim3(64 * NW), lds, st, a,
                      row_tiles, num_wgs);
@@ -750,6 +919,46 @@ hipError_t launch_dh(const AttnArgs& a, int kind, bool defer, int rb, int row_ti
 }
 
 }  // namespace
+
+namespace {
+
+template <int DH, int KIND>
+hipError_t launch_docpass_dh(const AttnArgs& a, const DocPassArgs& d, int num_work, int hkv, hipStream_t st) {
+  constexpr int NW = kDocPassLdsWaves;
+  constexpr int RB = kDocPassLdsRb;
+  constexpr int MAXS = LAZY_DOCPASS_STAGES;
+  constexpr int WPE = LAZY_DOCPASS_LDS_WPE;
+  using SG = StageGeom<DH, false, NW, MAXS>;
+  const size_t lds = (size_t)SG::kLdsTotal;
+  hipError_t e = ensure_lds_attr<docpass_kernel_ptr<DH, KIND, RB, NW, MAXS, WPE>>(lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((docpass_lds_kernel<DH, KIND, RB, NW, MAXS, WPE>), dim3((unsigned)hkv, (unsigned)num_work),
+                     dim3(64 * NW), lds, st, a, d);
+  return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_docpass_kind(const AttnArgs& a, const DocPassArgs& d, int kind, int num_work, int hkv,
+                               hipStream_t st) {
+  switch (kind) {
+    case kHalf:
+      return launch_docpass_dh<DH, kHalf>(a, d, num_work, hkv, st);
+    case kInter:
+      return launch_docpass_dh<DH, kInter>(a, d, num_work, hkv, st);
+    default:
+      return launch_docpass_dh<DH, kAlibi>(a, d, num_work, hkv, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_docpass_lds(const AttnArgs& a, const DocPassArgs& d, int kind, int head_dim, int num_work, int hkv,
+                              hipStream_t st) {
+  if (num_work <= 0) return hipSuccess;
+  if (head_dim == 128) return launch_docpass_kind<128>(a, d, kind, num_work, hkv, st);
+  if (head_dim == 64) return launch_docpass_kind<64>(a, d, kind, num_work, hkv, st);
+  return hipErrorNotSupported;
+}
 
 hipError_t launch_prefill_lds(const AttnArgs& a, int kind, bool defer, int head_dim, int rb, int row_tiles,
                               int splits, int num_reqs, int hkv, hipStream_t st) {

@@ -33,8 +33,9 @@ def _batch(rng, num_docs=12, R=7, max_docs=6, dup=True):
     return layouts, nb
 
 
-def _expected(layouts, kind, num_blocks, group, hkv, rb, min_readers):
-    """What the plan must contain, derived with plain loops."""
+def _expected(layouts, kind, num_blocks, group, hkv, rb, min_readers, few):
+    """What the plan must contain, derived with plain loops (few: the work-item count under which documents are
+    cut into chunks)."""
     key = lambda sg: (sg.blocks[0], sg.length)  # noqa: E731
     readers = {}
     for lay in layouts:
@@ -48,11 +49,11 @@ def _expected(layouts, kind, num_blocks, group, hkv, rb, min_readers):
                 first[key(sg)] = sg
     docs = sorted(first, key=lambda k: (-((first[k].length + 15) // 16) * readers[k], (k[0] << 32) | k[1]))
     index = {k: i for i, k in enumerate(docs)}
-    # chunks: only when the pass holds fewer than 1024 waves; then up to ceil(2048 / waves) even chunks of
-    # at least 32 tiles per document
+    # chunks: only when the pass holds fewer than `few` work items; then up to ceil(2 few / items) even chunks
+    # of at least 32 tiles per document
     ntiles = {k: (first[k].length + 15) // 16 for k in docs}
-    waves = hkv * sum(-(-readers[k] * group // (16 * rb)) for k in docs)
-    want = -(-2048 // waves) if 0 < waves < 1024 else 1
+    items = hkv * sum(-(-readers[k] * group // (16 * rb)) for k in docs)
+    want = -(-2 * few // items) if 0 < items < few else 1
     ct, nchunks = {}, {}
     for k in docs:
         n = max(1, min(want, ntiles[k] // 32))
@@ -85,29 +86,36 @@ def _expected(layouts, kind, num_blocks, group, hkv, rb, min_readers):
                                         max(1, sum(blocks_for(n) for n in f["seg_len"])))
     work = []
     for i, k in enumerate(docs):
-        rows = readers[k] * group
-        items = -(-rows // (16 * rb))
-        padded = items  # one doc-pass wave per workgroup: no padding
+        n_items = -(-readers[k] * group // (16 * rb))
         for c in range(nchunks[k]):
-            work += [(i, b * rb if b < items else (rows + 15) // 16, c, ct[k]) for b in range(padded)]
+            work += [(i, b * rb, c, ct[k]) for b in range(n_items)]
     return {"doc_tiles": doc_tiles, "doc_start": doc_start, "reads": reads, "req_reads": req_reads,
             "tiles": [int(w) for w in tiles], "tile_start": list(tstart), "ctx_tiles": list(nctx), "work": work}
 
 
+def _pass_shape(geom):
+    """(16-row blocks per work item, chunking threshold): bf16 runs the LDS-staged pass, a workgroup of 8 waves
+    x 16 rows per item; fp32 the per-wave pass, 2 (dh 128) or 4 (dh 64) row blocks per item."""
+    if geom.dtype == L.LAZY_BF16:
+        return 8, 256
+    return (2 if geom.head_dim == 128 else 4), 1024
+
+
 @pytest.mark.parametrize("seed", range(6))
 @pytest.mark.parametrize("kind", ["rope_half", "alibi"])
-def test_plan_matches_a_plain_derivation(seed, kind):
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_plan_matches_a_plain_derivation(seed, kind, dtype):
     rng = np.random.default_rng(seed)
     layouts, nb = _batch(rng)
-    geom = L.make_geom(8 if seed % 2 else 32, 2 if seed % 2 else 8, 128 if seed % 3 else 64, "bf16")
+    geom = L.make_geom(8 if seed % 2 else 32, 2 if seed % 2 else 8, 128 if seed % 3 else 64, dtype)
     group = geom.num_q_heads // geom.num_kv_heads
     f = flatten_layouts(layouts)
     min_readers = 2 + seed % 2
     h = L.build_shared_plan(geom, L.KIND_BY_NAME[kind], f["seg_start"], f["seg_len"], f["seg_pos0"],
                             f["seg_is_ctx"], f["seg_block_start"], f["blocks"], nb, 0, min_readers)
-    rb = h["row_blocks"]
-    assert rb == (2 if geom.head_dim == 128 else 4)
-    want = _expected(layouts, L.KIND_BY_NAME[kind], nb, group, geom.num_kv_heads, rb, min_readers)
+    rb, few = _pass_shape(geom)
+    assert h["row_blocks"] == rb
+    want = _expected(layouts, L.KIND_BY_NAME[kind], nb, group, geom.num_kv_heads, rb, min_readers, few)
     assert [int(w) for w in h["doc_tiles"]] == want["doc_tiles"]
     assert list(h["doc_tile_start"]) == want["doc_start"]
     got_reads = [[int(w) for w in h["reads"][h["read_start"][i]: h["read_start"][i + 1]]]
@@ -145,9 +153,10 @@ def test_plan_refusals():
                             fb["seg_block_start"], fb["blocks"], 8, 0, 2)
 
 
-def test_plan_chunks_few_long_documents():
-    """Three 4096-token documents read by 64 requests: the pass would hold 3 x 8 row-block groups of 256 tiles,
-    so each document is cut into chunks and each read takes one slot per chunk."""
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_plan_chunks_few_long_documents(dtype):
+    """Three 4096-token documents read by 64 requests: the pass would hold a few dozen (bf16) or a few hundred
+    (fp32) work items of 256 tiles, so each document is cut into chunks and each read takes one slot per chunk."""
     blocks = {d: list(range(256 * d, 256 * (d + 1))) for d in range(3)}
     layouts, nb = [], 768
     for r in range(64):
@@ -158,13 +167,16 @@ def test_plan_chunks_few_long_documents():
         segs.append(Segment([nb], 5, pos, False))
         nb += 1
         layouts.append(RequestLayout(segs))
-    geom = L.make_geom(32, 8, 128, "bf16")
+    geom = L.make_geom(32, 8, 128, dtype)
     f = flatten_layouts(layouts)
     h = L.build_shared_plan(geom, 0, f["seg_start"], f["seg_len"], f["seg_pos0"], f["seg_is_ctx"],
                             f["seg_block_start"], f["blocks"], nb, 0, 2)
     work = h["work"].reshape(-1, 4)
     assert h["num_docs"] == 3 and h["num_reads"] == 192
+    # bf16: 8 heads x 3 documents x 2 row tiles = 48 items < 256, want ceil(512 / 48) = 11 chunks, capped at
+    # 256 / 32 = 8; fp32: 8 x 3 x 8 = 192 waves < 1024, want 11, capped at 8
     assert set(work[:, 3].tolist()) == {32} and set(work[:, 2].tolist()) == set(range(8))
     assert list(h["req_reads"]) == [24] * 64  # 3 documents x 8 chunks
-    want = _expected(layouts, 0, nb, 4, 8, 2, 2)
+    rb, few = _pass_shape(geom)
+    want = _expected(layouts, 0, nb, 4, 8, rb, 2, few)
     assert [tuple(x) for x in work.tolist()] == want["work"]
