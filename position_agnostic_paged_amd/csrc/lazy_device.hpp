@@ -82,6 +82,15 @@ __device__ __forceinline__ typename Elem<T>::Frag4 load4(const T* p) {
   return *reinterpret_cast<const typename Elem<T>::Frag4*>(p);
 }
 
+// Cache-policy operand of a direct global->LDS copy with the nontemporal
+// (streaming) bit.  On MI355X a plain 2 GiB read stream of whole 1 KiB
+// wave-contiguous pieces measured 7.1-7.2 TB/s with it against 6.2-6.3
+// TB/s with the default policy, for register loads and for these copies
+// alike; reads of 64-byte row pieces (the decode kernel's K fragments) drop
+// to 5.9 TB/s with it, and data that other workgroups re-read through L2
+// loses its hits, so only the document pass's copies use it.
+constexpr int kCopyAuxStream = 2;
+
 // -------------------------------------------------------------- misc helpers
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
