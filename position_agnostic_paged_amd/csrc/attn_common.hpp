@@ -448,7 +448,7 @@ struct WaveAttn {
 #pragma unroll
       for (int c = 0; c < NC; ++c) f.k[x][c] = load8<T>(kp + 32 * c);
 #pragma unroll
-      for (int n = 0; n < NV; ++n) f.v[x][n] = load4<T>(vp + n * 16 * kBlock);
+      for (int n = 0; n < NV; ++n) f.v[x][n] = load4_stream<T>(vp + n * 16 * kBlock);
     }
   }
 

@@ -88,8 +88,18 @@ __device__ __forceinline__ typename Elem<T>::Frag4 load4(const T* p) {
 // TB/s with the default policy, for register loads and for these copies
 // alike; reads of 64-byte row pieces (the decode kernel's K fragments) drop
 // to 5.9 TB/s with it, and data that other workgroups re-read through L2
-// loses its hits, so only the document pass's copies use it.
+// loses its hits, so of the copies only the document pass's use it.
 constexpr int kCopyAuxStream = 2;
+
+// A V fragment load of the per-wave kernels with the nontemporal hint: each
+// instruction reads 16 channel rows x 32 bytes, whole lines, so the hint
+// pays (no-sharing 64 x 32K decode 1.335 -> 1.182 ms on MI355X, 6.3 -> 7.1
+// TB/s); where many requests re-read the same V through L2 it costs a few
+// percent (128 x 16K MQA decode over shared documents 0.142 -> 0.147 ms).
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::Frag4 load4_stream(const T* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const typename Elem<T>::Frag4*>(p));
+}
 
 // -------------------------------------------------------------- misc helpers
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
