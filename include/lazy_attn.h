@@ -247,7 +247,7 @@ lazy_status lazy_attn_decode(const lazy_geom* geom, const lazy_pos_desc* pos, co
                              void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /* Plan of a document-major decode (host; pure).  Input: the batch's segments
- * as for lazy_build_tiles.  A cached document read by >= min_readers (>= 2)
+ * as for lazy_build_tiles.  A cached document read by >= min_readers (>= 1)
  * context segments of the batch (one physical copy: same blocks wherever it
  * is read) is "shared": it gets one tile list at its local positions (tile
  * offset = local position of slot 0), and each of its reads a 64-bit read

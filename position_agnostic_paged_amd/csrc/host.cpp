@@ -274,7 +274,7 @@ extern "C" lazy_status lazy_build_shared_plan(
   if (st != LAZY_OK) return st;
   st = check_segments(kind, num_reqs, seg_start, seg_len, seg_pos0, seg_is_ctx, seg_block_start, blocks, num_blocks);
   if (st != LAZY_OK) return st;
-  if (min_readers < 2) return fail(LAZY_ERR_ARG, "min_readers must be >= 2 (got %d)", min_readers);
+  if (min_readers < 1) return fail(LAZY_ERR_ARG, "min_readers must be >= 1 (got %d)", min_readers);
   if (num_reqs > 65536) return fail(LAZY_ERR_UNSUPPORTED, "more than 65536 requests");
   if (!tile_start || !ctx_tiles || !doc_tile_start || !read_start || !req_reads || !counts_out)
     return fail(LAZY_ERR_ARG, "NULL output array");

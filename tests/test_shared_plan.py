@@ -110,7 +110,7 @@ def test_plan_matches_a_plain_derivation(seed, kind, dtype):
     geom = L.make_geom(8 if seed % 2 else 32, 2 if seed % 2 else 8, 128 if seed % 3 else 64, dtype)
     group = geom.num_q_heads // geom.num_kv_heads
     f = flatten_layouts(layouts)
-    min_readers = 2 + seed % 2
+    min_readers = 1 + seed % 3
     h = L.build_shared_plan(geom, L.KIND_BY_NAME[kind], f["seg_start"], f["seg_len"], f["seg_pos0"],
                             f["seg_is_ctx"], f["seg_block_start"], f["blocks"], nb, 0, min_readers)
     rb, few = _pass_shape(geom)
@@ -138,7 +138,7 @@ def test_plan_refusals():
     f = flatten_layouts(layouts)
     args = (f["seg_start"], f["seg_len"], f["seg_pos0"], f["seg_is_ctx"], f["seg_block_start"], f["blocks"])
     with pytest.raises(L.LazyError, match="min_readers"):
-        L.build_shared_plan(geom, 0, *args, nb, 0, 1)
+        L.build_shared_plan(geom, 0, *args, nb, 0, 0)
     with pytest.raises(L.LazyError, match="outside the pool"):
         L.build_shared_plan(geom, 0, *args, 3, 0, 2)
     far = max(s.pos0 for lay in layouts for s in lay.segments if s.ctx and s.length)
