@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ tile_start, int32_t num_reqs,
                                                       int32_t hq, int32_t rows_bound, int32_t max_splits,
                                                       int32_t chunk, const int32_t* __restrict__ extra_n,
-                                                      int32_t extra_base) {
+                                                      int32_t extra_base, const bf16* __restrict__ extra_o) {
   // RPB rows per workgroup; per row, TPR threads cover the channels (4 each)
   // and NG groups of them take every NG-th split, so the partial loads of
   // many splits are in flight together (NG = 1 for few splits); the groups'
@@ -247,7 +247,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int s = grp; s < ns + ne; s += NG) {
     const int64_t pr = (int64_t)(s < ns ? s : extra_base + (s - ns)) * rows_bound + row;
     const float ms = part_ml[pr * 2], ls = part_ml[pr * 2 + 1];
-    const f32x4 os = *reinterpret_cast<const f32x4*>(part_o + pr * DH + c4);
+    f32x4 os;
+    if (extra_o != nullptr && s >= ns) {  // a bf16 accumulator of the document pass
+      const bf16x4 e = *reinterpret_cast<const bf16x4*>(extra_o + ((int64_t)(s - ns) * rows_bound + row) * DH + c4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) os[j] = (float)e[j];
+    } else {
+      os = *reinterpret_cast<const f32x4*>(part_o + pr * DH + c4);
+    }
     const float mn = fmaxf(M, ms);
     const float a = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mn);
     const float b = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - mn);
@@ -460,7 +467,8 @@ hipError_t dispatch_kind(int kind, bool defer, const AttnArgs& a, const Plan& p,
 
 template <typename T, int DH>
 hipError_t launch_combine(const AttnArgs& a, const Plan& p, const int32_t* q_start, int num_reqs, hipStream_t st,
-                          const int32_t* extra_n = nullptr, int extra_base = 0, int max_extra = 0) {
+                          const int32_t* extra_n = nullptr, int extra_base = 0, int max_extra = 0,
+                          const bf16* extra_o = nullptr) {
   // many partials per row: one row per workgroup, 256 / (DH/4) split groups;
   // few: rows side by side
   constexpr int NGMAX = 256 / (DH / 4);
@@ -468,13 +476,13 @@ hipError_t launch_combine(const AttnArgs& a, const Plan& p, const int32_t* q_sta
     dim3 grid((unsigned)p.rows_bound);
     hipLaunchKernelGGL((combine_kernel<T, DH, NGMAX>), grid, dim3(256), 0, st, a.part_o, a.part_ml,
                        reinterpret_cast<T*>(a.out), q_start, a.tile_start, num_reqs, a.hq, p.rows_bound, p.splits,
-                       p.chunk, extra_n, extra_base);
+                       p.chunk, extra_n, extra_base, extra_o);
   } else {
     constexpr int RPB = NGMAX;
     dim3 grid((unsigned)((p.rows_bound + RPB - 1) / RPB));
     hipLaunchKernelGGL((combine_kernel<T, DH, 1>), grid, dim3(256), 0, st, a.part_o, a.part_ml,
                        reinterpret_cast<T*>(a.out), q_start, a.tile_start, num_reqs, a.hq, p.rows_bound, p.splits,
-                       p.chunk, extra_n, extra_base);
+                       p.chunk, extra_n, extra_base, extra_o);
   }
   return hipGetLastError();
 }
@@ -748,9 +756,20 @@ extern "C" lazy_status lazy_attn_decode_noalloc(const lazy_geom* geom, const laz
 namespace lazy {
 namespace {
 
+// Workspace of the document-major decode: (m, l) of every partial slot in
+// fp32; the split slots' accumulators in fp32; the document pass's slots'
+// accumulators in the call's dtype (bf16 halves the pass's partial traffic,
+// written once and read once by the combine, for a rounding like the
+// output's own).
+size_t shared_ws_doc_bytes(const lazy_geom* g, const Plan& p, int max_req_reads) {
+  const size_t esz = g->dtype == LAZY_BF16 ? 2 : 4;
+  return (size_t)max_req_reads * (size_t)p.rows_bound * (size_t)g->head_dim * esz;
+}
+
 size_t shared_ws_bytes(const lazy_geom* g, const Plan& p, int max_req_reads) {
-  const size_t per = (size_t)g->head_dim + 2;
-  return (size_t)(p.splits + max_req_reads) * (size_t)p.rows_bound * per * sizeof(float) + 256;
+  const size_t split_o = (size_t)p.splits * (size_t)p.rows_bound * (size_t)g->head_dim * sizeof(float);
+  const size_t ml = (size_t)(p.splits + max_req_reads) * (size_t)p.rows_bound * 2 * sizeof(float);
+  return split_o + ((shared_ws_doc_bytes(g, p, max_req_reads) + 255) & ~(size_t)255) + ml + 512;
 }
 
 template <typename T, int DH>
@@ -773,7 +792,9 @@ hipError_t run_shared(const lazy_pos_desc* pd, const AttnArgs& a, const DocPassA
     if (e != hipSuccess) return e;
   }
   // 3. per (request, head): the request's split partials and its reads' partials
-  return launch_combine<T, DH>(a, p, nullptr, num_reqs, st, req_reads, d.slot_base, max_req_reads);
+  const bf16* doc_o = nullptr;
+  if constexpr (std::is_same<T, bf16>::value) doc_o = reinterpret_cast<const bf16*>(d.doc_o);
+  return launch_combine<T, DH>(a, p, nullptr, num_reqs, st, req_reads, d.slot_base, max_req_reads, doc_o);
 }
 
 }  // namespace
@@ -837,9 +858,16 @@ extern "C" lazy_status lazy_attn_decode_shared(
   a.rows_bound = p.rows_bound;
   a.max_q_len = 1;
   a.force_partials = 1;
-  a.part_o = reinterpret_cast<float*>(workspace);
-  a.part_ml = a.part_o + (size_t)(p.splits + max_req_reads) * p.rows_bound * geom->head_dim;
+  // workspace: split accumulators (fp32) | document-pass accumulators (dtype)
+  // | (m, l) of every slot; the document pass's slots are split slots
+  // slot_base.. in part_ml and doc_o's own rows (fp32: they continue part_o)
+  unsigned char* wsb = reinterpret_cast<unsigned char*>(workspace);
+  const size_t split_o = (size_t)p.splits * p.rows_bound * geom->head_dim * sizeof(float);
+  const size_t doc_bytes = (shared_ws_doc_bytes(geom, p, max_req_reads) + 255) & ~(size_t)255;
+  a.part_o = reinterpret_cast<float*>(wsb);
+  a.part_ml = reinterpret_cast<float*>(wsb + split_o + doc_bytes);
   DocPassArgs d{};
+  d.doc_o = wsb + split_o;
   d.doc_tiles = doc_tiles;
   d.doc_tile_start = doc_tile_start;
   d.read_start = read_start;

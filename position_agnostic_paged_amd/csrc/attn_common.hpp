@@ -104,7 +104,10 @@ struct DocPassArgs {
   const int32_t* read_start;      // [num_docs + 1]
   const uint64_t* reads;          // [num_reads]
   const int32_t* work;            // [num_work][4]: (doc, first 16-row block, chunk, tiles per chunk)
-  int32_t slot_base;              // partial slots of a request's reads start at slot_base
+  int32_t slot_base;              // partial slots of a request's reads start at slot_base (in part_ml)
+  // the reads' accumulators, [max_req_reads][rows_bound][dh] in the call's
+  // dtype (fp32: the rows right after the split slots' part_o rows)
+  void* doc_o;
 };
 
 __device__ __forceinline__ void unpack_read(uint64_t w, int& req, int& slot, int& delta) {

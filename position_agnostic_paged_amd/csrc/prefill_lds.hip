@@ -757,7 +757,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
 // (m, l, acc) partial in its read's slot (one per chunk), which the decode
 // combine merges with the request's other partials.  Grid (KV head, work
 // item): with eight KV heads a head is one XCD, and a document's row tiles
-// are adjacent items there, so the second one finds the tiles in L2.
+// are adjacent items there, so the second one finds the tiles in L2.  The
+// accumulators go out in bf16 (DocPassArgs::doc_o), m and l in fp32.
 template <int DH, int KIND, int RB, int NW, int MAXS, int WPE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) void docpass_lds_kernel(
     AttnArgs a, DocPassArgs d) {
@@ -830,12 +831,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     if ((rb0 + b) * 16 + r >= nrows) continue;
-    float* po = a.part_o + prow[b] * DH + 4 * g;
+    // the accumulator in bf16 in the reads' own rows; (m, l) in fp32 in the
+    // slot's part_ml row
+    bf16* po = reinterpret_cast<bf16*>(d.doc_o) + (prow[b] - (int64_t)d.slot_base * a.rows_bound) * DH + 4 * g;
     if (bad[b]) {
-      constexpr uint32_t kQNaN = 0x7FC00000u;
-      const u32x4 nan4 = {kQNaN, kQNaN, kQNaN, kQNaN};
+      constexpr uint32_t kQNaN = 0x7FC00000u, kQNaN2 = 0x7FC07FC0u;
+      const u32x2 nan_o = {kQNaN2, kQNaN2};
 #pragma unroll
-      for (int n = 0; n < NV; ++n) *reinterpret_cast<u32x4*>(po + 16 * n) = nan4;
+      for (int n = 0; n < NV; ++n) *reinterpret_cast<u32x2*>(po + 16 * n) = nan_o;
       if (g == 0) {
         const u32x2 nan2 = {kQNaN, kQNaN};
         *reinterpret_cast<u32x2*>(a.part_ml + prow[b] * 2) = nan2;
@@ -843,7 +846,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
       continue;
     }
 #pragma unroll
-    for (int n = 0; n < NV; ++n) *reinterpret_cast<f32x4*>(po + 16 * n) = acc[b][n];
+    for (int n = 0; n < NV; ++n) {
+      bf16x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = (bf16)acc[b][n][j];
+      *reinterpret_cast<bf16x4*>(po + 16 * n) = w;
+    }
     if (g == 0) {
       a.part_ml[prow[b] * 2 + 0] = m_run[b];
       a.part_ml[prow[b] * 2 + 1] = lsum[b][0];

@@ -350,9 +350,10 @@ class Engine:
     def doc_major_pays(self) -> bool:
         """Whether the document-major decode is the faster one for this geometry: with a query group of up to
         16 heads a wave's row blocks hold several reads of a shared document, so its tiles are read once for
-        all of them.  A larger group (Falcon's 71 heads per KV head) fills a wave's rows with one read, the
-        pass then shares nothing and only adds partials (measured on MI355X: 128 x 16K MQA decode 0.141 ms per
-        request vs 0.241 ms document-major; 48 x 8K-66K GQA-8 decode 0.81 vs 0.38 ms)."""
+        all of them.  A larger group (Falcon's 71 heads per KV head) fills the rows with one read each, the
+        pass then shares little and adds partials (measured on MI355X: 128 x 16K MQA decode over shared
+        documents 0.148 ms per request vs 0.203 ms document-major; 48 x 8K-66K GQA-8 decode 0.81 vs 0.26
+        ms)."""
         return self.hq // self.hkv <= 16
 
     def shared_plan(self, layouts: Sequence[RequestLayout], min_readers: int = 1) -> SharedPlan:
