@@ -88,6 +88,9 @@ class StepUploads:
         self.host = [torch.empty(capacity, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
         self.host_np = [h.numpy() for h in self.host]
         self.dev = torch.empty(capacity, dtype=torch.uint8, device=self.device)
+        # the buffer seen as each staged dtype, so a staged array's view is one slice (capacity and every
+        # offset are multiples of 8 bytes)
+        self.dev_as = {dt: self.dev.view(tdt) for dt, tdt in TORCH_INT.items()}
         self.done: List[Optional[torch.cuda.Event]] = [None, None]
         self.cur = 1
         self.items: List[Tuple[int, np.dtype, Tuple[int, ...]]] = []
@@ -108,7 +111,7 @@ class StepUploads:
         if off + a.nbytes > self.cap:
             raise ValueError(f"step metadata exceeds {self.cap} bytes")
         self.host_np[self.cur][off: off + a.nbytes] = a.reshape(-1).view(np.uint8)
-        self.items.append((off, a.dtype, a.shape))
+        self.items.append((off, np.dtype(a.dtype), a.shape))
         self.off = off + a.nbytes
         return len(self.items) - 1
 
@@ -124,9 +127,11 @@ class StepUploads:
         self.done[self.cur] = ev
         views = []
         for off, dt, shape in self.items:
-            tdt = TORCH_INT[np.dtype(dt)]
-            nb = int(np.prod(shape)) * np.dtype(dt).itemsize
-            views.append(self.dev[off: off + nb].view(tdt).view(shape))
+            first = off // dt.itemsize
+            if len(shape) == 1:
+                views.append(self.dev_as[dt][first: first + shape[0]])
+            else:
+                views.append(self.dev_as[dt][first: first + int(np.prod(shape))].view(shape))
         for fn in self.callbacks:
             fn(views)
         return views
@@ -174,6 +179,7 @@ class SharedPlan:
                                 f["seg_is_ctx"], f["seg_block_start"], f["blocks"], engine.num_blocks,
                                 engine.pos.table_rows, min_readers)
         self.host = h
+        self.ws_bytes = None  # the decode's workspace bytes, asked for once
         self.num_reqs = len(layouts)
         for k in ("num_docs", "num_reads", "num_work", "max_req_reads", "total_tiles", "max_tiles", "row_blocks"):
             setattr(self, k, int(h[k]))
@@ -370,8 +376,10 @@ class Engine:
         """Decode with every shared document read once for all its readers (lazy_attn_decode_shared)."""
         if out is None:
             out = torch.empty_like(q)
-        ws = self._workspace(L.decode_shared_workspace_size(self.geom, plan.num_reqs, plan.max_tiles, plan.total_tiles,
-                                                            plan.max_req_reads))
+        if plan.ws_bytes is None:
+            plan.ws_bytes = L.decode_shared_workspace_size(self.geom, plan.num_reqs, plan.max_tiles,
+                                                           plan.total_tiles, plan.max_req_reads)
+        ws = self._workspace(plan.ws_bytes)
         L.attn_decode_shared(self.geom, self.pos.c, self.k_cache, self.v_cache, self.num_blocks, plan.tiles,
                              plan.tile_start, plan.ctx_tiles, plan.max_tiles, plan.total_tiles, plan.doc_tiles,
                              plan.doc_tile_start, plan.read_start, plan.reads, plan.req_reads, plan.work,

@@ -106,7 +106,9 @@ def _check(st: int):
 
 
 def _np_ptr(a: Optional[np.ndarray]):
-    return None if a is None else a.ctypes.data_as(C.c_void_p)
+    # the address as a plain int (every pointer parameter is declared c_void_p); the int keeps no
+    # reference, so every caller passes an array it holds in a local until the call returns
+    return None if a is None else a.ctypes.data
 
 
 def _dev(t) -> Optional[int]:
