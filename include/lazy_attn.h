@@ -84,6 +84,14 @@ typedef enum {
 
 /* Flags in lazy_pos_desc.flags. */
 #define LAZY_FLAG_PREROTATED 1u /* control build: context K already at global positions, no deferral */
+/* Prefill: the tile lists come from lazy_build_tiles_paired (no tile pair
+ * spans two documents, or a document and the private tokens), so the query
+ * is rotated once per document (by -Delta, [N] "Key designs": the single
+ * relative rotation, here on the query side as the decode applies it)
+ * instead of each K tile pair in LDS.  A list without that property gives
+ * wrong attention for the pairs that span a boundary; without the flag the
+ * prefill rotates K and takes any list. */
+#define LAZY_FLAG_DOC_PAIRS 2u
 
 #define LAZY_BLOCK_SIZE 16
 #define LAZY_MAX_BLOCK_ID ((1 << 24) - 1)
@@ -171,6 +179,18 @@ lazy_status lazy_build_tiles(int32_t kind, int32_t num_reqs, const int32_t* seg_
                              const int64_t* seg_pos0, const uint8_t* seg_is_ctx, const int32_t* seg_block_start,
                              const int32_t* blocks, int64_t num_blocks, int32_t max_pos, uint64_t* tiles_out,
                              int64_t tiles_cap, int32_t* tile_start, int32_t* ctx_tiles);
+
+/* As lazy_build_tiles, with every context segment of an odd tile count
+ * closed by one empty tile (block 0, mask 0, the segment's offset), so that
+ * each tile pair (2i, 2i+1) of a request lies within one document or within
+ * the private tokens: the layout the prefill's per-document query rotation
+ * (LAZY_FLAG_DOC_PAIRS) reads.  tiles_cap must allow one extra tile per
+ * context segment; ctx_tiles counts the empty tiles. */
+lazy_status lazy_build_tiles_paired(int32_t kind, int32_t num_reqs, const int32_t* seg_start,
+                                    const int32_t* seg_len, const int64_t* seg_pos0, const uint8_t* seg_is_ctx,
+                                    const int32_t* seg_block_start, const int32_t* blocks, int64_t num_blocks,
+                                    int32_t max_pos, uint64_t* tiles_out, int64_t tiles_cap, int32_t* tile_start,
+                                    int32_t* ctx_tiles);
 
 /* ------------------------------------------------------------- device calls */
 

@@ -610,6 +610,7 @@ extern "C" lazy_status lazy_attn_prefill(const lazy_geom* geom, const lazy_pos_d
   a.group = group;
   a.rows_bound = p.rows_bound;
   a.max_q_len = max_q_len;
+  a.doc_pairs = (pos->flags & LAZY_FLAG_DOC_PAIRS) ? 1 : 0;
   if (need > 0) {
     a.part_o = reinterpret_cast<float*>(workspace);
     a.part_ml = a.part_o + (size_t)p.splits * p.rows_bound * geom->head_dim;

@@ -92,6 +92,7 @@ struct AttnArgs {
   int32_t rows_bound;  // partial row stride: (max query rows) * hq
   int32_t max_q_len;   // prefill: rows per request covered by the grid
   int32_t force_partials;  // write (m, l, acc) partials even with one split (a later combine merges more)
+  int32_t doc_pairs;       // prefill: no tile pair spans two documents (LAZY_FLAG_DOC_PAIRS)
 };
 
 // The document-major pass of a decode batch: each shared document's tiles

@@ -50,7 +50,8 @@ lazy_status check_pos(const lazy_geom* g, const lazy_pos_desc* p) {
   if (!p) return fail(LAZY_ERR_ARG, "pos descriptor is NULL");
   if (p->kind != LAZY_ROPE_HALF && p->kind != LAZY_ROPE_INTERLEAVED && p->kind != LAZY_ALIBI)
     return fail(LAZY_ERR_ARG, "unknown positional kind %d", p->kind);
-  if (p->flags & ~LAZY_FLAG_PREROTATED) return fail(LAZY_ERR_ARG, "unknown flags 0x%x", p->flags);
+  if (p->flags & ~(LAZY_FLAG_PREROTATED | LAZY_FLAG_DOC_PAIRS))
+    return fail(LAZY_ERR_ARG, "unknown flags 0x%x", p->flags);
   if (!(p->softmax_scale > 0.f) || !isfinite(p->softmax_scale))
     return fail(LAZY_ERR_ARG, "softmax_scale must be finite and > 0");
   if (p->kind == LAZY_ALIBI) {
@@ -229,11 +230,12 @@ lazy_status emit_segment(int32_t kind, int s, const int32_t* seg_len, const int6
 }  // namespace
 }  // namespace lazy
 
-extern "C" lazy_status lazy_build_tiles(int32_t kind, int32_t num_reqs, const int32_t* seg_start,
-                                        const int32_t* seg_len, const int64_t* seg_pos0, const uint8_t* seg_is_ctx,
-                                        const int32_t* seg_block_start, const int32_t* blocks, int64_t num_blocks,
-                                        int32_t max_pos, uint64_t* tiles_out, int64_t tiles_cap,
-                                        int32_t* tile_start, int32_t* ctx_tiles) {
+namespace {
+
+lazy_status build_tiles(int32_t kind, int32_t num_reqs, const int32_t* seg_start, const int32_t* seg_len,
+                        const int64_t* seg_pos0, const uint8_t* seg_is_ctx, const int32_t* seg_block_start,
+                        const int32_t* blocks, int64_t num_blocks, int32_t max_pos, bool align_pairs,
+                        uint64_t* tiles_out, int64_t tiles_cap, int32_t* tile_start, int32_t* ctx_tiles) {
   clear_error();
   lazy_status st = check_segments(kind, num_reqs, seg_start, seg_len, seg_pos0, seg_is_ctx, seg_block_start, blocks,
                                   num_blocks);
@@ -253,6 +255,15 @@ extern "C" lazy_status lazy_build_tiles(int32_t kind, int32_t num_reqs, const in
       st = emit_segment(kind, s, seg_len, seg_pos0, seg_is_ctx, seg_block_start, blocks, num_blocks, max_pos,
                         tiles_out, tiles_cap, nt);
       if (st != LAZY_OK) return st;
+      if (ctx && align_pairs && ((nt - before) & 1)) {
+        // one empty tile (mask 0, block 0, the segment's offset) closes the
+        // document's last pair
+        if (nt >= tiles_cap) return fail(LAZY_ERR_ARG, "tile capacity %lld too small", (long long)tiles_cap);
+        const int64_t nblk = nt - before;
+        const int64_t off = kind != LAZY_ALIBI ? seg_pos0[s] : seg_pos0[s] + (int64_t)LAZY_BLOCK_SIZE * nblk;
+        if (off > LAZY_MAX_OFFSET) return fail(LAZY_ERR_ARG, "segment %d: offset %lld exceeds 2^24-1", s, (long long)off);
+        tiles_out[nt++] = (uint64_t)off << 16;
+      }
       if (ctx) nctx += nt - before;
     }
     ctx_tiles[r] = (int32_t)nctx;
@@ -260,6 +271,27 @@ extern "C" lazy_status lazy_build_tiles(int32_t kind, int32_t num_reqs, const in
   if (nt > INT32_MAX) return fail(LAZY_ERR_ARG, "too many tiles");
   tile_start[num_reqs] = (int32_t)nt;
   return LAZY_OK;
+}
+
+}  // namespace
+
+extern "C" lazy_status lazy_build_tiles(int32_t kind, int32_t num_reqs, const int32_t* seg_start,
+                                        const int32_t* seg_len, const int64_t* seg_pos0, const uint8_t* seg_is_ctx,
+                                        const int32_t* seg_block_start, const int32_t* blocks, int64_t num_blocks,
+                                        int32_t max_pos, uint64_t* tiles_out, int64_t tiles_cap,
+                                        int32_t* tile_start, int32_t* ctx_tiles) {
+  return build_tiles(kind, num_reqs, seg_start, seg_len, seg_pos0, seg_is_ctx, seg_block_start, blocks, num_blocks,
+                     max_pos, false, tiles_out, tiles_cap, tile_start, ctx_tiles);
+}
+
+extern "C" lazy_status lazy_build_tiles_paired(int32_t kind, int32_t num_reqs, const int32_t* seg_start,
+                                               const int32_t* seg_len, const int64_t* seg_pos0,
+                                               const uint8_t* seg_is_ctx, const int32_t* seg_block_start,
+                                               const int32_t* blocks, int64_t num_blocks, int32_t max_pos,
+                                               uint64_t* tiles_out, int64_t tiles_cap, int32_t* tile_start,
+                                               int32_t* ctx_tiles) {
+  return build_tiles(kind, num_reqs, seg_start, seg_len, seg_pos0, seg_is_ctx, seg_block_start, blocks, num_blocks,
+                     max_pos, true, tiles_out, tiles_cap, tile_start, ctx_tiles);
 }
 
 extern "C" lazy_status lazy_build_shared_plan(

@@ -91,20 +91,27 @@ __device__ __forceinline__ void wait_stages(int n) {
   }
 }
 
-template <int DH, bool ROT, int NW, int MAXS = 10>
+// ROT: each stage's K tiles are rotated in LDS (two cos/sin rows per stage);
+// QROT: the query is rotated per document (one cos/sin row per stage, the
+// pair's); RESERVE bytes after the ring hold the waves' raw query rows.
+template <int DH, bool ROT, int NW, int MAXS = 10, bool QROT = false, int RESERVE = 0>
 struct StageGeom {
   static constexpr int kTile = kBlock * DH * 2;      // bytes of one 16 x dh bf16 tile
   static constexpr int kChunksPerRow = DH / 8;       // 16-byte chunks in a K row
   static constexpr int kK = 0;                       // two K tiles
   static constexpr int kV = 2 * kTile;               // two V tiles
-  static constexpr int kCS = 4 * kTile;              // two cos/sin rows (fp32 [dh])
-  static constexpr int kHdr = kCS + (ROT ? 2 * DH * 4 : 0);  // the pair's decoded tile words (PairHdr)
+  static constexpr int kCS = 4 * kTile;              // cos/sin rows (fp32 [dh] each)
+  static constexpr int kCsRows = ROT ? 2 : (QROT ? 1 : 0);
+  static constexpr int kHdr = kCS + kCsRows * DH * 4;  // the pair's decoded tile words (PairHdr)
   static constexpr int kBytes = kHdr + 32;
   static constexpr int kKChunks = 2 * kTile / 16;    // 16-B chunks of the K pair (same for V)
   static constexpr int kCopies = 2 * kKChunks / (NW * 64);  // K + V copies per thread
-  static constexpr int kLoads = kCopies + (ROT ? 1 : 0);    // copies per wave per stage
-  static constexpr int kStages = (kLdsBytes / kBytes) < MAXS ? (kLdsBytes / kBytes) : MAXS;
-  static constexpr int kLdsTotal = kStages * kBytes;
+  static constexpr int kLoads = kCopies + (kCsRows > 0 ? 1 : 0);  // copies per wave per stage
+  static constexpr int kRing = kLdsBytes - RESERVE;
+  static constexpr int kStages = (kRing / kBytes) < MAXS ? (kRing / kBytes) : MAXS;
+  static constexpr int kReserve = kStages * kBytes;  // offset of the reserved bytes
+  static constexpr int kLdsTotal = kStages * kBytes + RESERVE;
+  static_assert(!(ROT && QROT), "one rotation side");
   // Pairs past the consumed one that each iteration waits for: with the K
   // rotation, pair p + 2 (rotated during iteration p); without it, pair
   // p + 1 (its scores end iteration p), which leaves one more stage in flight
@@ -174,14 +181,18 @@ __device__ __forceinline__ void xcd_unit(int wg, int num_wgs, int splits, int hk
   row_tile = t;
 }
 
-template <int DH, int KIND, bool DEFER, int RB, int NW, int MAXS = 10, bool NT = false>
+template <int DH, int KIND, bool DEFER, int RB, int NW, int MAXS = 10, bool NT = false, bool QROT = false>
 struct LdsPrefill {
   using F8 = bf16x8;
   using F4 = bf16x4;
   static constexpr int NC = DH / 32;  // contraction chunks of QK^T
   static constexpr int NV = DH / 16;  // 16-channel blocks of the output
-  static constexpr bool kRot = (KIND != kAlibi) && DEFER;
-  using SG = StageGeom<DH, kRot, NW, MAXS>;
+  // kRot: K rotated by Delta in LDS per pair; kQRot: the query rotated by
+  // -Delta once per document (the tile lists keep each pair in one document)
+  static constexpr bool kRot = (KIND != kAlibi) && DEFER && !QROT;
+  static constexpr bool kQRot = (KIND != kAlibi) && DEFER && QROT;
+  static constexpr int kQBytes = RB * NC * 64 * 16;  // one wave's raw query fragments
+  using SG = StageGeom<DH, kRot, NW, MAXS, kQRot, kQRot ? NW * kQBytes : 0>;
   static constexpr int S = SG::kStages;
 
   const AttnArgs& a;
@@ -255,6 +266,17 @@ struct LdsPrefill {
         delta[x] = 0;
       }
     }
+    if (kQRot) {
+      // one rotation per pair: tile 0's document offset (0 for private
+      // tokens, whose keys and query both sit at global positions)
+      int d = priv[0] ? 0 : mt[0].offset;
+      if (d >= a.max_pos) {  // outside the table: drop the pair
+        mt[0].mask = mt[1].mask = 0u;
+        d = 0;
+      }
+      delta[0] = d;
+      delta[1] = 0;
+    }
   }
 
   // copy pair q into its stage buffer (every wave issues SG::kLoads copies)
@@ -276,9 +298,10 @@ struct LdsPrefill {
                          ((int64_t)blk * a.hkv + kvh) * (int64_t)(kBlock * DH * 2);
       __builtin_amdgcn_global_load_lds(base + copy_off[i], st + cb * 16, 16, 0, NT ? kCopyAuxStream : 0);
     }
-    if (kRot) {
-      // the two cos/sin rows: DH/4 chunks each; wave w copies its share (lane-masked)
-      constexpr int kCsChunks = 2 * (DH / 4);
+    if constexpr (SG::kCsRows > 0) {
+      // the cos/sin rows (two: the tiles' offsets; one: the pair's): DH/4
+      // chunks each; wave w copies its share (lane-masked)
+      constexpr int kCsChunks = SG::kCsRows * (DH / 4);
       constexpr int kPerWave = kCsChunks / NW;
       static_assert(kPerWave >= 1 && kCsChunks <= 64, "cos/sin copy shape");
       if (lane >= wave * kPerWave && lane < (wave + 1) * kPerWave) {
@@ -397,6 +420,64 @@ struct LdsPrefill {
     rot_store(rot_load(q, delta));
   }
 
+  // The wave's raw query fragments (global positions) in its reserved LDS
+  // bytes, and their rotation by -Delta of pair q's document into qw, with
+  // the pair's cos/sin row from its stage (the decode's query rotation,
+  // applied once per document change).
+  __device__ __forceinline__ uint32_t q_slot(int b, int c) const {
+    return (uint32_t)(SG::kReserve + wave * kQBytes + ((b * NC + c) * 64 + lane) * 16);
+  }
+  __device__ __forceinline__ void store_q(const F8 (&qr)[RB][NC]) const {
+#pragma unroll
+    for (int b = 0; b < RB; ++b)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) *reinterpret_cast<F8*>(lds + q_slot(b, c)) = qr[b][c];
+  }
+  __device__ __forceinline__ void rotate_q(int q, F8 (&qw)[RB][NC]) const {
+    const float* cs = reinterpret_cast<const float*>(stage(q) + SG::kCS);
+    const int g = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      if (KIND == kHalf) {
+#pragma unroll
+        for (int c = 0; c < NC / 2; ++c) {
+          const F8 lo = *reinterpret_cast<const F8*>(lds + q_slot(b, c));
+          const F8 hi = *reinterpret_cast<const F8*>(lds + q_slot(b, c + NC / 2));
+          const int k0 = 32 * c + 8 * g;
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs + k0), c1 = *reinterpret_cast<const f32x4*>(cs + k0 + 4);
+          const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + DH / 2 + k0);
+          const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + DH / 2 + k0 + 4);
+          F8 nlo, nhi;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float co = t < 4 ? c0[t & 3] : c1[t & 3], si = t < 4 ? s0[t & 3] : s1[t & 3];
+            const float x1 = (float)lo[t], x2 = (float)hi[t];
+            nlo[t] = (bf16)(x1 * co + x2 * si);
+            nhi[t] = (bf16)(x2 * co - x1 * si);
+          }
+          qw[b][c] = nlo;
+          qw[b][c + NC / 2] = nhi;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const F8 x = *reinterpret_cast<const F8*>(lds + q_slot(b, c));
+          const int k0 = 16 * c + 4 * g;
+          const f32x4 co = *reinterpret_cast<const f32x4*>(cs + k0);
+          const f32x4 si = *reinterpret_cast<const f32x4*>(cs + DH / 2 + k0);
+          F8 n;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float x1 = (float)x[2 * u], x2 = (float)x[2 * u + 1];
+            n[2 * u] = (bf16)(x1 * co[u] + x2 * si[u]);
+            n[2 * u + 1] = (bf16)(x2 * co[u] - x1 * si[u]);
+          }
+          qw[b][c] = n;
+        }
+      }
+    }
+  }
+
   // Raw scores of a pair's two tiles (K rows at their global positions):
   // s[h][b][j] = score of query row r of block b against the key whose
   // product row the lane's koff[h] selects.
@@ -426,12 +507,12 @@ struct LdsPrefill {
 // reference maxima.  qp is each row's query position and slope_raw its ALiBi
 // slope over the softmax scale (masking: causal against private tiles, the
 // bias against every tile).
-template <int DH, int KIND, bool DEFER, int RB, int NW, int MAXS, bool NT>
-__device__ __forceinline__ void lds_attend(LdsPrefill<DH, KIND, DEFER, RB, NW, MAXS, NT>& pl,
-                                           const typename LdsPrefill<DH, KIND, DEFER, RB, NW, MAXS, NT>::F8 (&qr)[RB][DH / 32],
+template <int DH, int KIND, bool DEFER, int RB, int NW, int MAXS, bool NT, bool QROT>
+__device__ __forceinline__ void lds_attend(LdsPrefill<DH, KIND, DEFER, RB, NW, MAXS, NT, QROT>& pl,
+                                           const typename LdsPrefill<DH, KIND, DEFER, RB, NW, MAXS, NT, QROT>::F8 (&qr_in)[RB][DH / 32],
                                            const int (&qp)[RB], const float (&slope_raw)[RB], bool has_rows,
                                            f32x4 (&acc)[RB][DH / 16], f32x4 (&lsum)[RB], float (&m_run)[RB]) {
-  using P = LdsPrefill<DH, KIND, DEFER, RB, NW, MAXS, NT>;
+  using P = LdsPrefill<DH, KIND, DEFER, RB, NW, MAXS, NT, QROT>;
   using F8 = typename P::F8;
   constexpr int NC = P::NC;
   constexpr int NV = P::NV;
@@ -443,6 +524,18 @@ __device__ __forceinline__ void lds_attend(LdsPrefill<DH, KIND, DEFER, RB, NW, M
   const int wave = uniform((int)__builtin_amdgcn_workitem_id_x() >> 6);
   const int npairs = pl.npairs;
   const int r = lane & 15, g = lane >> 4;
+  // the query fragments the products use; with the per-document query
+  // rotation, the raw ones (global positions) wait in LDS and these hold
+  // them rotated by -Delta of the current document
+  F8 qr[RB][NC];
+#pragma unroll
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qr[b][c] = qr_in[b][c];
+  if constexpr (P::kQRot) {
+    if (has_rows) pl.store_q(qr);
+  }
+  int dq_cur = 0;  // the query's current rotation (0: raw)
 
   // Fragment offsets inside a stage (loop-invariant).  K product h, chunk c:
   // row r of the product is key (tile r/8, token 8 ((r/4)%2) + 4h + r%4), so
@@ -502,6 +595,13 @@ __device__ __forceinline__ void lds_attend(LdsPrefill<DH, KIND, DEFER, RB, NW, M
     dr[0] = uniform((int)d[0]);
     dr[1] = uniform((int)d[1]);
   }
+  if constexpr (P::kQRot) {
+    // the first pair's document (its stage landed before the barrier above;
+    // the query's own LDS writes are this wave's and need no barrier)
+    const int d0 = uniform((int)pl.read_deltas(0)[0]);
+    if (has_rows && d0 != 0) pl.rotate_q(0, qr);
+    dq_cur = d0;
+  }
   wait_lgkm0();  // the rotated rows of pairs 0 and 1 are written before the barrier publishes them
   asm volatile("s_barrier" ::: "memory");
   f32x4 s[2][RB];
@@ -525,6 +625,9 @@ __device__ __forceinline__ void lds_attend(LdsPrefill<DH, KIND, DEFER, RB, NW, M
     const u32x4 hv_next = pl.read_hdr(p + 1);
     u32x2 dv_next = {0u, 0u};
     if constexpr (P::kRot) dv_next = pl.read_deltas(p + 3);
+    // the next pair's document offset (the per-document query rotation)
+    int dq_next = dq_cur;
+    if constexpr (P::kQRot) dq_next = (p + 1 < npairs) ? uniform((int)pl.read_deltas(p + 1)[0]) : dq_cur;
     // Rotation of pair p + 2 in two halves: its LDS reads now, its
     // arithmetic and write-back (with the next copies) in the other half of
     // the iteration from this pair's softmax and products.
@@ -626,6 +729,22 @@ __device__ __forceinline__ void lds_attend(LdsPrefill<DH, KIND, DEFER, RB, NW, M
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int j = 0; j < 4; ++j) pf[b][4 * h + j] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[h][b][j], sl, negm[b]));
+      if constexpr (P::kQRot) {
+        // a new document from the next pair on: the query rotated for it
+        // before the next pair's scores (its stage and cos/sin row landed
+        // before this iteration's barrier)
+        if (dq_next != dq_cur) {
+          if (dq_next == 0) {
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+#pragma unroll
+              for (int c = 0; c < NC; ++c) qr[b][c] = *reinterpret_cast<const F8*>(pl.lds + pl.q_slot(b, c));
+          } else {
+            pl.rotate_q(p + 1, qr);
+          }
+          dq_cur = dq_next;
+        }
+      }
       pl.scores(pl.stage(p + 1), koff, qr, s);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -649,9 +768,9 @@ __device__ __forceinline__ void lds_attend(LdsPrefill<DH, KIND, DEFER, RB, NW, M
   }
 }
 
-template <int DH, int KIND, bool DEFER, int RB, int NW>
+template <int DH, int KIND, bool DEFER, int RB, int NW, bool QROT>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int row_tiles, int num_wgs) {
-  using P = LdsPrefill<DH, KIND, DEFER, RB, NW>;
+  using P = LdsPrefill<DH, KIND, DEFER, RB, NW, 10, false, QROT>;
   using F8 = typename P::F8;
   using F4 = typename P::F4;
   constexpr int NC = P::NC;
@@ -712,7 +831,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_lds_kernel(AttnArgs a, int
   f32x4 acc[RB][NV];
   f32x4 lsum[RB];
   float m_run[RB];
-  lds_attend<DH, KIND, DEFER, RB, NW, 10, false>(pl, qr, qp, slope_raw, has_rows, acc, lsum, m_run);
+  lds_attend<DH, KIND, DEFER, RB, NW, 10, false, QROT>(pl, qr, qp, slope_raw, has_rows, acc, lsum, m_run);
   if (!has_rows) return;
 
   // O[row r][16n + 4g + j] = acc[b][n][j]: normalised output (one split) or an
@@ -826,7 +945,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE))) 
   f32x4 acc[RB][NV];
   f32x4 lsum[RB];
   float m_run[RB];
-  lds_attend<DH, KIND, false, RB, NW, MAXS, true>(pl, qr, qp, slope_raw, has_rows, acc, lsum, m_run);
+  lds_attend<DH, KIND, false, RB, NW, MAXS, true, false>(pl, qr, qp, slope_raw, has_rows, acc, lsum, m_run);
   if (!has_rows) return;
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
@@ -879,9 +998,9 @@ hipError_t ensure_lds_attr(size_t lds) {
   return hipSuccess;
 }
 
-template <int DH, int KIND, bool DEFER, int RB, int NW>
+template <int DH, int KIND, bool DEFER, int RB, int NW, bool QROT>
 const void* prefill_kernel_ptr() {
-  return reinterpret_cast<const void*>(&prefill_lds_kernel<DH, KIND, DEFER, RB, NW>);
+  return reinterpret_cast<const void*>(&prefill_lds_kernel<DH, KIND, DEFER, RB, NW, QROT>);
 }
 
 template <int DH, int KIND, int RB, int NW, int MAXS, int WPE>
@@ -889,41 +1008,44 @@ const void* docpass_kernel_ptr() {
   return reinterpret_cast<const void*>(&docpass_lds_kernel<DH, KIND, RB, NW, MAXS, WPE>);
 }
 
-template <int DH, int KIND, bool DEFER, int RB>
+template <int DH, int KIND, bool DEFER, int RB, bool QROT>
 hipError_t launch_rb(const AttnArgs& a, int row_tiles, int splits, int num_reqs, int hkv, hipStream_t st) {
   constexpr int NW = kPrefillWaves;
-  constexpr bool rot = (KIND != kAlibi) && DEFER;
-  using SG = StageGeom<DH, rot, NW>;
+  using SG = typename LdsPrefill<DH, KIND, DEFER, RB, NW, 10, false, QROT>::SG;
   const size_t lds = (size_t)SG::kLdsTotal;
-  hipError_t e = ensure_lds_attr<prefill_kernel_ptr<DH, KIND, DEFER, RB, NW>>(lds);
+  hipError_t e = ensure_lds_attr<prefill_kernel_ptr<DH, KIND, DEFER, RB, NW, QROT>>(lds);
   if (e != hipSuccess) return e;
   const int num_wgs = row_tiles * splits * hkv * num_reqs;  // 1-D: the kernel maps ids to units
-  hipLaunchKernelGGL((prefill_lds_kernel<DH, KIND, DEFER, RB, NW>), dim3((unsigned)num_wgs), dim3(64 * NW), lds, st, a,
-                     row_tiles, num_wgs);
+  hipLaunchKernelGGL((prefill_lds_kernel<DH, KIND, DEFER, RB, NW, QROT>), dim3((unsigned)num_wgs), dim3(64 * NW), lds,
+                     st, a, row_tiles, num_wgs);
   return hipGetLastError();
 }
 
 // rows per workgroup = 16 x rb x 4 (the host plan's row tile) = NW waves x (4 rb / NW) blocks
-template <int DH, int KIND, bool DEFER>
+template <int DH, int KIND, bool DEFER, bool QROT>
 hipError_t launch_kind(const AttnArgs& a, int rb, int row_tiles, int splits, int num_reqs, int hkv, hipStream_t st) {
   constexpr int NW = kPrefillWaves;
   static_assert(NW == 4 || NW == 8, "waves per workgroup");
-  return rb == 4 ? launch_rb<DH, KIND, DEFER, 16 / NW>(a, row_tiles, splits, num_reqs, hkv, st)
-                 : launch_rb<DH, KIND, DEFER, 8 / NW>(a, row_tiles, splits, num_reqs, hkv, st);
+  return rb == 4 ? launch_rb<DH, KIND, DEFER, 16 / NW, QROT>(a, row_tiles, splits, num_reqs, hkv, st)
+                 : launch_rb<DH, KIND, DEFER, 8 / NW, QROT>(a, row_tiles, splits, num_reqs, hkv, st);
 }
 
+// qrot: the tile pairs keep to one document (LAZY_FLAG_DOC_PAIRS): the query
+// is rotated per document instead of K per pair
 template <int DH>
-hipError_t launch_dh(const AttnArgs& a, int kind, bool defer, int rb, int row_tiles, int splits, int num_reqs,
-                     int hkv, hipStream_t st) {
+hipError_t launch_dh(const AttnArgs& a, int kind, bool defer, bool qrot, int rb, int row_tiles, int splits,
+                     int num_reqs, int hkv, hipStream_t st) {
   switch (kind) {
     case kHalf:
-      return defer ? launch_kind<DH, kHalf, true>(a, rb, row_tiles, splits, num_reqs, hkv, st)
-                   : launch_kind<DH, kHalf, false>(a, rb, row_tiles, splits, num_reqs, hkv, st);
+      if (!defer) return launch_kind<DH, kHalf, false, false>(a, rb, row_tiles, splits, num_reqs, hkv, st);
+      return qrot ? launch_kind<DH, kHalf, true, true>(a, rb, row_tiles, splits, num_reqs, hkv, st)
+                  : launch_kind<DH, kHalf, true, false>(a, rb, row_tiles, splits, num_reqs, hkv, st);
     case kInter:
-      return defer ? launch_kind<DH, kInter, true>(a, rb, row_tiles, splits, num_reqs, hkv, st)
-                   : launch_kind<DH, kInter, false>(a, rb, row_tiles, splits, num_reqs, hkv, st);
+      if (!defer) return launch_kind<DH, kInter, false, false>(a, rb, row_tiles, splits, num_reqs, hkv, st);
+      return qrot ? launch_kind<DH, kInter, true, true>(a, rb, row_tiles, splits, num_reqs, hkv, st)
+                  : launch_kind<DH, kInter, true, false>(a, rb, row_tiles, splits, num_reqs, hkv, st);
     default:
-      return launch_kind<DH, kAlibi, false>(a, rb, row_tiles, splits, num_reqs, hkv, st);
+      return launch_kind<DH, kAlibi, false, false>(a, rb, row_tiles, splits, num_reqs, hkv, st);
   }
 }
 
@@ -971,10 +1093,11 @@ hipError_t launch_docpass_lds(const AttnArgs& a, const DocPassArgs& d, int kind,
 
 hipError_t launch_prefill_lds(const AttnArgs& a, int kind, bool defer, int head_dim, int rb, int row_tiles,
                               int splits, int num_reqs, int hkv, hipStream_t st) {
+  const bool qrot = a.doc_pairs != 0;
   if (rb != 2 && rb != 4) return hipErrorNotSupported;
   if (kind != kAlibi && defer && a.cos_sin == nullptr) return hipErrorNotSupported;  // rows come from the table
-  if (head_dim == 128) return launch_dh<128>(a, kind, defer, rb, row_tiles, splits, num_reqs, hkv, st);
-  if (head_dim == 64) return launch_dh<64>(a, kind, defer, rb, row_tiles, splits, num_reqs, hkv, st);
+  if (head_dim == 128) return launch_dh<128>(a, kind, defer, qrot, rb, row_tiles, splits, num_reqs, hkv, st);
+  if (head_dim == 64) return launch_dh<64>(a, kind, defer, qrot, rb, row_tiles, splits, num_reqs, hkv, st);
   return hipErrorNotSupported;
 }
 

@@ -47,6 +47,7 @@ class PosDesc:
         self.softmax_scale = L.softmax_scale(head_dim, yarn_factor if kind != "alibi" else 1.0)
         self.c = L.PosDescC(self.kind_id, L.LAZY_FLAG_PREROTATED if prerotated else 0, max_pos,
                             self.softmax_scale, L._dev(self.table), L._dev(self.inv_freq), L._dev(self.slopes))
+        self._variants = {}
 
     @property
     def table_rows(self) -> int:
@@ -62,9 +63,16 @@ class PosDesc:
         if lo < 0 or hi >= limit:
             raise ValueError(f"rotation positions [{lo}, {hi}] outside [0, {limit})")
 
-    def with_flags(self, prerotated: bool) -> L.PosDescC:
-        c = L.PosDescC.from_buffer_copy(self.c)
-        c.flags = L.LAZY_FLAG_PREROTATED if prerotated else 0
+    def with_flags(self, prerotated: bool, doc_pairs: bool = False) -> L.PosDescC:
+        """The descriptor with the given flags (one copy per combination, kept): prerotated = the control
+        on keys stored at global positions; doc_pairs = the prefill's tile lists keep each tile pair within
+        one document (lazy_build_tiles_paired), so it rotates the query per document."""
+        key = (bool(prerotated), bool(doc_pairs))
+        c = self._variants.get(key)
+        if c is None:
+            c = L.PosDescC.from_buffer_copy(self.c)
+            c.flags = (L.LAZY_FLAG_PREROTATED if prerotated else 0) | (L.LAZY_FLAG_DOC_PAIRS if doc_pairs else 0)
+            self._variants[key] = c
         return c
 
 
@@ -145,11 +153,13 @@ class TileTable:
     its own, or staged into a step's ``StepUploads``)."""
 
     def __init__(self, layouts: Sequence[RequestLayout], kind_id: int, num_blocks: int, device,
-                 uploads: Optional[StepUploads] = None, max_pos: int = 0):
+                 uploads: Optional[StepUploads] = None, max_pos: int = 0, paired: bool = False):
         f = flatten_layouts(layouts)
         cap = sum(blocks_for(n) for n in f["seg_len"]) or 1
         tiles, tstart, nctx = L.build_tiles(kind_id, f["seg_start"], f["seg_len"], f["seg_pos0"], f["seg_is_ctx"],
-                                            f["seg_block_start"], f["blocks"] or [0], num_blocks, cap, max_pos)
+                                            f["seg_block_start"], f["blocks"] or [0], num_blocks, cap, max_pos,
+                                            paired)
+        self.paired = paired
         self.host_tiles, self.host_start, self.host_ctx = tiles, tstart, nctx
         self.num_reqs = len(layouts)
         self.max_tiles = int(np.max(np.diff(tstart))) if len(layouts) else 0
@@ -337,17 +347,27 @@ class Engine:
     # list each request's cached documents most shared first (paging.order_for_reuse)
     order_for_reuse = True
 
-    def tile_table(self, layouts: Sequence[RequestLayout], uploads: Optional[StepUploads] = None) -> TileTable:
+    def tile_table(self, layouts: Sequence[RequestLayout], uploads: Optional[StepUploads] = None,
+                   paired: bool = False) -> TileTable:
+        """Tile lists of a batch; paired (prefill): every document closed to whole tile pairs, so the prefill
+        rotates the query once per document instead of every K pair."""
         if self.order_for_reuse:
             layouts = order_for_reuse(layouts)
-        return TileTable(layouts, self.pos.kind_id, self.num_blocks, self.device, uploads, self.pos.table_rows)
+        return TileTable(layouts, self.pos.kind_id, self.num_blocks, self.device, uploads, self.pos.table_rows,
+                         paired)
+
+    # prefill tile lists closed to whole pairs per document (the query rotated per document: on MI355X the
+    # 70B-shape prefill call measured against the K-rotating kernel; see the prefill notes)
+    prefill_pairs = True
 
     def prefill(self, tt: TileTable, q: torch.Tensor, q_start: torch.Tensor, q_pos0: torch.Tensor, max_q_len: int,
                 out: Optional[torch.Tensor] = None, pos: Optional[L.PosDescC] = None, stream=None) -> torch.Tensor:
         if out is None:
             out = torch.empty_like(q)
         ws = self._workspace(L.workspace_size(self.geom, tt.num_reqs, max_q_len, tt.max_tiles, tt.total_tiles, True))
-        L.attn_prefill(self.geom, self.pos.c if pos is None else pos, self.k_cache, self.v_cache, self.num_blocks,
+        if pos is None:
+            pos = self.pos.with_flags(False, tt.paired)
+        L.attn_prefill(self.geom, pos, self.k_cache, self.v_cache, self.num_blocks,
                        tt.tiles, tt.tile_start, tt.ctx_tiles, q, q_start, q_pos0, tt.num_reqs, max_q_len, tt.max_tiles,
                        tt.total_tiles, out, ws, stream)
         return out

@@ -25,6 +25,7 @@ LAZY_OK, LAZY_ERR_ARG, LAZY_ERR_UNSUPPORTED, LAZY_ERR_WORKSPACE, LAZY_ERR_HIP = 
 LAZY_BF16, LAZY_FP32 = 0, 1
 LAZY_ROPE_HALF, LAZY_ROPE_INTERLEAVED, LAZY_ALIBI = 0, 1, 2
 LAZY_FLAG_PREROTATED = 1
+LAZY_FLAG_DOC_PAIRS = 2
 BLOCK_SIZE = 16
 
 KIND_BY_NAME = {"rope_half": LAZY_ROPE_HALF, "rope_interleaved": LAZY_ROPE_INTERLEAVED, "alibi": LAZY_ALIBI}
@@ -32,7 +33,7 @@ KIND_BY_NAME = {"rope_half": LAZY_ROPE_HALF, "rope_interleaved": LAZY_ROPE_INTER
 EXPORTED = [
     "lazy_rope_freqs", "lazy_softmax_scale", "lazy_rope_table", "lazy_alibi_slopes", "lazy_pack_tiles",
     "lazy_unpack_tiles",
-    "lazy_build_tiles", "lazy_kv_write", "lazy_attn_workspace_size", "lazy_attn_prefill", "lazy_attn_decode",
+    "lazy_build_tiles", "lazy_build_tiles_paired", "lazy_kv_write", "lazy_attn_workspace_size", "lazy_attn_prefill", "lazy_attn_decode",
     "lazy_attn_decode_noalloc", "lazy_build_shared_plan", "lazy_attn_decode_shared_workspace_size",
     "lazy_attn_decode_shared", "lazy_debug_unpack", "lazy_last_error",
 ]
@@ -72,6 +73,7 @@ def lib() -> C.CDLL:
             "lazy_pack_tiles": [P, P, P, I64, P],
             "lazy_unpack_tiles": [P, I64, P, P, P],
             "lazy_build_tiles": [I32, I32, P, P, P, P, P, P, I64, I32, P, I64, P, P],
+            "lazy_build_tiles_paired": [I32, I32, P, P, P, P, P, P, I64, I32, P, I64, P, P],
             "lazy_kv_write": [P, P, P, P, I64, P, P, P, P, P, I32, P],
             "lazy_attn_prefill": [P, P, P, P, I64, P, P, P, P, P, P, I32, I32, I32, I64, P, P, C.c_size_t, P],
             "lazy_attn_decode": [P, P, P, P, I64, P, P, P, P, P, I32, I32, I64, P, P, C.c_size_t, P],
@@ -178,9 +180,10 @@ def unpack_tiles(words):
 
 
 def build_tiles(kind: int, seg_start, seg_len, seg_pos0, seg_is_ctx, seg_block_start, blocks, num_blocks: int,
-                tiles_cap: Optional[int] = None, max_pos: int = 0):
+                tiles_cap: Optional[int] = None, max_pos: int = 0, paired: bool = False):
     """Tile words, tile_start [R+1], ctx_tiles [R] of every request (host arrays); max_pos > 0 checks every
-    rotary document offset against the cos/sin table's rows."""
+    rotary document offset against the cos/sin table's rows; paired: lazy_build_tiles_paired (documents
+    closed to whole tile pairs; tiles_cap grows by one per context segment)."""
     ss = np.ascontiguousarray(seg_start, np.int32)
     sl = np.ascontiguousarray(seg_len, np.int32)
     sp = np.ascontiguousarray(seg_pos0, np.int64)
@@ -189,12 +192,14 @@ def build_tiles(kind: int, seg_start, seg_len, seg_pos0, seg_is_ctx, seg_block_s
     bl = np.ascontiguousarray(blocks, np.int32)
     R = ss.shape[0] - 1
     cap = int(tiles_cap if tiles_cap is not None else max(1, bl.shape[0]))
+    if paired:
+        cap += int(np.count_nonzero(sc))
     tiles = np.empty(cap, np.uint64)
     tstart = np.empty(R + 1, np.int32)
     nctx = np.empty(max(R, 1), np.int32)
-    _check(lib().lazy_build_tiles(kind, R, _np_ptr(ss), _np_ptr(sl), _np_ptr(sp), _np_ptr(sc), _np_ptr(sb),
-                                  _np_ptr(bl), num_blocks, max_pos, _np_ptr(tiles), cap, _np_ptr(tstart),
-                                  _np_ptr(nctx)))
+    fn = lib().lazy_build_tiles_paired if paired else lib().lazy_build_tiles
+    _check(fn(kind, R, _np_ptr(ss), _np_ptr(sl), _np_ptr(sp), _np_ptr(sc), _np_ptr(sb), _np_ptr(bl), num_blocks,
+              max_pos, _np_ptr(tiles), cap, _np_ptr(tstart), _np_ptr(nctx)))
     return tiles[: tstart[R]].copy(), tstart, nctx[:R].copy()
 
 

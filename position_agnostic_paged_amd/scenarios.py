@@ -165,13 +165,13 @@ class PrefillScenario(_Base):
             layouts.append(RequestLayout(segs))
             qpos0.append(ctx_len)
         self.layouts = layouts
-        self.tt = engine.tile_table(layouts)
+        self.tt = engine.tile_table(layouts, paired=engine.prefill_pairs)
         self.q_start = torch.from_numpy(self.q_start_h).to(self.dev)
         self.q_pos0 = torch.tensor(qpos0, dtype=torch.int32, device=self.dev)
         self.out = torch.empty_like(self.q)
 
     def run(self, stream=None) -> torch.Tensor:
-        pos = self.eng.pos.with_flags(self.prerotated)
+        pos = self.eng.pos.with_flags(self.prerotated, self.tt.paired)
         return self.eng.prefill(self.tt, self.q, self.q_start, self.q_pos0, self.max_q_len, out=self.out, pos=pos,
                                 stream=stream)
 

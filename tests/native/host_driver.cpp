@@ -98,6 +98,15 @@ int main() {
     CHECK(lazy_build_tiles(trial % 3, R, seg_start.data(), seg_len.data(), seg_pos0.data(), seg_ctx.data(),
                            seg_bs.data(), bl, 500, 0, out.data(), tiles, tstart.data(), nctx.data()) == LAZY_OK);
     CHECK(tstart[R] == tiles);
+    {  // documents closed to whole tile pairs: every request's context tile count even
+      std::vector<uint64_t> outp(tiles + seg_len.size() + 1);
+      CHECK(lazy_build_tiles_paired(trial % 3, R, seg_start.data(), seg_len.data(), seg_pos0.data(), seg_ctx.data(),
+                                    seg_bs.data(), bl, 500, 0, outp.data(), (int64_t)outp.size(), tstart.data(),
+                                    nctx.data()) == LAZY_OK);
+      for (int r = 0; r < R; ++r) CHECK(nctx[r] % 2 == 0);
+      CHECK(lazy_build_tiles(trial % 3, R, seg_start.data(), seg_len.data(), seg_pos0.data(), seg_ctx.data(),
+                             seg_bs.data(), bl, 500, 0, out.data(), tiles, tstart.data(), nctx.data()) == LAZY_OK);
+    }
     if (tiles > 0) {
       CHECK(lazy_build_tiles(trial % 3, R, seg_start.data(), seg_len.data(), seg_pos0.data(), seg_ctx.data(),
                              seg_bs.data(), bl, 500, 0, out.data(), tiles - 1, tstart.data(), nctx.data()) ==

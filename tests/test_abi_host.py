@@ -250,3 +250,44 @@ def test_device_calls_validate_before_launch(L):
     assert noalloc(g, p, 0, 64, 0) == L.LAZY_OK
     assert noalloc(g, p, 4096, 20000, 4096 * 100) == L.LAZY_ERR_WORKSPACE
     assert "static scratch" in L.last_error()
+
+
+def test_paired_tiles_keep_each_pair_in_one_document():
+    """lazy_build_tiles_paired: the plain list with one empty tile (mask 0) after every context segment of an
+    odd tile count, so each pair (2i, 2i+1) of a request lies within one document or within its private
+    tokens; ctx_tiles counts the empty tiles."""
+    import numpy as np
+
+    from position_agnostic_paged_amd import lazy_attn as LA
+
+    rng = np.random.default_rng(5)
+    for kind in (0, 1, 2):
+        seg_start, seg_len, seg_pos0, seg_ctx, seg_bs, blocks = [0], [], [], [], [0], []
+        nb = 0
+        for r in range(6):
+            pos = 0
+            for d in range(int(rng.integers(0, 5))):
+                n = int(rng.integers(1, 70))
+                seg_len.append(n); seg_pos0.append(pos); seg_ctx.append(1)
+                blocks += list(range(nb, nb + (n + 15) // 16)); nb += (n + 15) // 16; seg_bs.append(len(blocks))
+                pos += n
+            n = int(rng.integers(0, 40))
+            seg_len.append(n); seg_pos0.append(pos); seg_ctx.append(0)
+            blocks += list(range(nb, nb + (n + 15) // 16)); nb += (n + 15) // 16; seg_bs.append(len(blocks))
+            seg_start.append(len(seg_len))
+        args = (seg_start, seg_len, seg_pos0, seg_ctx, seg_bs, blocks or [0], max(nb, 1))
+        plain, ps, pc = LA.build_tiles(kind, *args)
+        paired, qs, qc = LA.build_tiles(kind, *args, paired=True)
+        b, o, m = LA.unpack_tiles(paired)
+        for r in range(6):
+            segs = range(seg_start[r], seg_start[r + 1])
+            want = []
+            for s in segs:
+                nt = (seg_len[s] + 15) // 16
+                want += [int(w) for w in plain[ps[r] + sum((seg_len[t] + 15) // 16 for t in segs if t < s):][:nt]]
+                if seg_ctx[s] and nt % 2:
+                    off = seg_pos0[s] if kind != 2 else seg_pos0[s] + 16 * nt
+                    want.append(off << 16)  # block 0, mask 0
+            assert [int(w) for w in paired[qs[r]: qs[r + 1]]] == want
+            nctx = sum((seg_len[s] + 15) // 16 + ((seg_len[s] + 15) // 16) % 2 for s in segs if seg_ctx[s])
+            assert qc[r] == nctx and nctx % 2 == 0

@@ -35,17 +35,20 @@ def _wl(key_or_wl):
 # ------------------------------------------------------------------------------------------ prefill
 
 def run_prefill(wl, variants):
-    """GPU prefill outputs per variant (shared, prerotated, on_the_fly), each on its own engine."""
+    """GPU prefill outputs per variant (shared, prerotated, on_the_fly[, paired]), each on its own engine;
+    paired (default True): tile lists closed to whole pairs per document, the query rotated per document;
+    False: plain tile lists, K rotated per pair in LDS."""
     from position_agnostic_paged_amd.scenarios import PrefillScenario
 
     outs = {}
-    for shared, prerotated, on_the_fly in variants:
+    for v in variants:
+        shared, prerotated, on_the_fly = v[:3]
         eng = _engine(wl, shared, on_the_fly=on_the_fly)
+        eng.prefill_pairs = v[3] if len(v) > 3 else True
         sc = PrefillScenario(wl, eng, shared=shared, prerotated=prerotated)
         out = sc.run().float().cpu().numpy()
         torch.cuda.synchronize()
-        outs[(shared, prerotated, on_the_fly)] = [out[sc.q_start_h[i]: sc.q_start_h[i + 1]]
-                                                  for i in range(len(sc.reqs))]
+        outs[tuple(v)] = [out[sc.q_start_h[i]: sc.q_start_h[i + 1]] for i in range(len(sc.reqs))]
         del sc, eng
         torch.cuda.empty_cache()
     return outs
@@ -121,6 +124,9 @@ NOSHARE = (False, False, False)
 ON_THE_FLY = (True, False, True)
 DOC_MAJOR = (True, False, False, True)  # decode: shared documents once for all their readers
 DOC_MAJOR_FLY = (True, False, True, True)
+# prefill: plain tile lists, K rotated per tile pair in LDS (the other prefill variants keep each tile pair
+# within one document and rotate the query per document)
+KROT = (True, False, False, False)
 
 
 # ---------------------------------------------------------------------------------------- the tests
@@ -147,11 +153,11 @@ def test_tiny_fp32_decode_document_major_two_orders():
 def test_llama8b_prefill_and_controls():
     """Config 2 (8 x (10 Zipf docs of 200 tokens + 32-token question), GQA 32/8) through the staged
     kernel, the in-kernel sincos path, and the no-sharing layout with and without deferral."""
-    check_prefill("llama8b_prefill", variants=(SHARED, ON_THE_FLY, NOSHARE, NOSHARE_PREROT))
+    check_prefill("llama8b_prefill", variants=(SHARED, KROT, ON_THE_FLY, NOSHARE, NOSHARE_PREROT))
 
 
 def test_llama8b_prefill_interleaved():
-    check_prefill("llama8b_prefill_interleaved", variants=(SHARED, NOSHARE_PREROT))
+    check_prefill("llama8b_prefill_interleaved", variants=(SHARED, KROT, NOSHARE_PREROT))
 
 
 def test_llama8b_decode_every_request_and_prerotated_control():
@@ -184,7 +190,7 @@ def test_falcon_alibi_decode_every_request():
 
 def test_ragged_prefill():
     """Questions of 1..64 tokens (two row tiles), a request with no document, 1..999-token documents."""
-    check_prefill("ragged", variants=(SHARED, NOSHARE_PREROT))
+    check_prefill("ragged", variants=(SHARED, KROT, NOSHARE_PREROT))
 
 
 def test_ragged_decode_uneven_splits():
@@ -211,7 +217,7 @@ def test_mixed_yarn_prefill_and_prerotated_control():
 
     wl = gen._mixed_llama70b(num_steps=1)
     wl.decode_reqs = []
-    check_prefill(wl, variants=(SHARED, NOSHARE, NOSHARE_PREROT))
+    check_prefill(wl, variants=(SHARED, KROT, NOSHARE, NOSHARE_PREROT))
 
 
 def test_mixed_yarn_decode_every_request():
@@ -228,7 +234,7 @@ def test_pages_overhead_shape_prefill():
     prefill shared, and the no-sharing layout with and without deferral (the overhead A/B pair)."""
     wl = make_workload("pages_overhead")
     wl.decode_reqs = []
-    check_prefill(wl, variants=(SHARED, NOSHARE, NOSHARE_PREROT))
+    check_prefill(wl, variants=(SHARED, KROT, NOSHARE, NOSHARE_PREROT))
 
 
 def test_pages_overhead_shape_decode():
@@ -247,7 +253,7 @@ def test_falcon_alibi_prefill_mqa_dh64():
 def test_dh64_interleaved_prefill_decode_and_control():
     """dh 64 interleaved RoPE through the staged prefill (K rotated in LDS), the decode kernel and the
     pre-rotated control on the no-sharing layout."""
-    check_prefill("small_dh64_interleaved", variants=(SHARED, NOSHARE_PREROT))
+    check_prefill("small_dh64_interleaved", variants=(SHARED, KROT, NOSHARE_PREROT))
     check_decode("small_dh64_interleaved", steps=[0, 1, 2, 3], variants=(SHARED, NOSHARE_PREROT, DOC_MAJOR))
 
 
