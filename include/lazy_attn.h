@@ -241,7 +241,7 @@ size_t lazy_attn_workspace_size(const lazy_geom* geom, int32_t num_reqs, int32_t
  * tile's Delta inside the kernel).  With LAZY_FLAG_DOC_PAIRS in pos->flags
  * (tile lists from lazy_build_tiles_paired) the bf16 kernel applies that
  * rotation to the query instead, once per document (q rotated by -Delta,
- * the same result); without it, to each K tile pair. */
+ * the same result); without it, to each K tile pair.
  * Host sizing hints: max_q_len >= every request's query count (required);
  * max_tiles ~ the largest tile count and total_tiles ~ tile_start[num_reqs]
  * (0 = unknown) size the split-K plan: each request gets one split per
