@@ -235,7 +235,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
     req = lo;
   }
-  const int ns = request_splits(tile_start[req + 1] - tile_start[req], chunk, max_splits);
+  // max_splits 0: no split partials (a document-major decode with no own tiles)
+  const int ns = max_splits > 0 ? request_splits(tile_start[req + 1] - tile_start[req], chunk, max_splits) : 0;
   // One pass: each group merges its splits into a running (m, l, o),
   // rescaling when the maximum grows, so every partial load is independent
   // of the others (an empty split, m = -inf, has weight 0).
@@ -776,11 +777,19 @@ size_t shared_ws_bytes(const lazy_geom* g, const Plan& p, int max_req_reads) {
 template <typename T, int DH>
 hipError_t run_shared(const lazy_pos_desc* pd, const AttnArgs& a, const DocPassArgs& d, const Plan& p, int rb,
                       int num_work, int num_reqs, int hkv, const int32_t* req_reads, int max_req_reads,
-                      hipStream_t st) {
-  // 1. each request's own tiles (private tokens, unshared documents), split-K
-  //    as usual, always into partials
-  hipError_t e = dispatch_kind<T, DH, false>(pd->kind, true, a, p, num_reqs, hkv, st);
-  if (e != hipSuccess) return e;
+                      int64_t total_tiles, hipStream_t st) {
+  // 1. each request's own tiles (unshared documents, private tokens), split-K
+  //    as usual, always into partials; none when every one of them went to
+  //    the pass (a plan with min_readers 1): no launch, and the combine
+  //    reads no split partials
+  Plan pc = p;
+  hipError_t e = hipSuccess;
+  if (total_tiles > 0) {
+    e = dispatch_kind<T, DH, false>(pd->kind, true, a, p, num_reqs, hkv, st);
+    if (e != hipSuccess) return e;
+  } else {
+    pc.splits = 0;
+  }
   // 2. every shared document once for all its readers
   if (num_work > 0) {
     AttnArgs ad = a;
@@ -795,7 +804,7 @@ hipError_t run_shared(const lazy_pos_desc* pd, const AttnArgs& a, const DocPassA
   // 3. per (request, head): the request's split partials and its reads' partials
   const bf16* doc_o = nullptr;
   if constexpr (std::is_same<T, bf16>::value) doc_o = reinterpret_cast<const bf16*>(d.doc_o);
-  return launch_combine<T, DH>(a, p, nullptr, num_reqs, st, req_reads, d.slot_base, max_req_reads, doc_o);
+  return launch_combine<T, DH>(a, pc, nullptr, num_reqs, st, req_reads, d.slot_base, max_req_reads, doc_o);
 }
 
 }  // namespace
@@ -880,12 +889,12 @@ extern "C" lazy_status lazy_attn_decode_shared(
   hipError_t e;
   if (geom->dtype == LAZY_BF16)
     e = geom->head_dim == 128
-            ? run_shared<bf16, 128>(pos, a, d, p, rb, num_work, num_reqs, hkv, req_reads, max_req_reads, s)
-            : run_shared<bf16, 64>(pos, a, d, p, rb, num_work, num_reqs, hkv, req_reads, max_req_reads, s);
+            ? run_shared<bf16, 128>(pos, a, d, p, rb, num_work, num_reqs, hkv, req_reads, max_req_reads, total_tiles, s)
+            : run_shared<bf16, 64>(pos, a, d, p, rb, num_work, num_reqs, hkv, req_reads, max_req_reads, total_tiles, s);
   else
     e = geom->head_dim == 128
-            ? run_shared<float, 128>(pos, a, d, p, rb, num_work, num_reqs, hkv, req_reads, max_req_reads, s)
-            : run_shared<float, 64>(pos, a, d, p, rb, num_work, num_reqs, hkv, req_reads, max_req_reads, s);
+            ? run_shared<float, 128>(pos, a, d, p, rb, num_work, num_reqs, hkv, req_reads, max_req_reads, total_tiles, s)
+            : run_shared<float, 64>(pos, a, d, p, rb, num_work, num_reqs, hkv, req_reads, max_req_reads, total_tiles, s);
   if (e != hipSuccess) return fail(LAZY_ERR_HIP, "shared-document decode launch failed: %s", hipGetErrorString(e));
   (void)num_docs;
   return LAZY_OK;

@@ -340,6 +340,17 @@ extern "C" lazy_status lazy_build_shared_plan(
     doc_of[k] = -1;
     docs.push_back({k, s, n, 0});
   }
+  // with min_readers 1 every request's private tokens become one more item
+  // of the pass too (read once, at Delta 0: keys and query both at global
+  // positions), so the split-K pass has nothing left to do
+  const bool private_items = min_readers == 1;
+  auto private_key = [](int s) -> uint64_t { return (1ull << 63) | (uint64_t)(uint32_t)s; };
+  if (private_items)
+    for (int s = 0; s < nseg; ++s) {
+      if (seg_is_ctx[s] || seg_len[s] <= 0) continue;
+      doc_of[private_key(s)] = -1;
+      docs.push_back({private_key(s), s, 1, 0});
+    }
   std::sort(docs.begin(), docs.end(), [&](const Doc& a, const Doc& b) {
     const int64_t wa = (int64_t)(seg_len[a.first_seg] + 15) / 16 * a.readers;
     const int64_t wb = (int64_t)(seg_len[b.first_seg] + 15) / 16 * b.readers;
@@ -349,10 +360,12 @@ extern "C" lazy_status lazy_build_shared_plan(
   for (size_t i = 0; i < docs.size(); ++i) doc_of[docs[i].key] = (int32_t)i;
 
   // 3. each shared document's tiles, at local positions (offset = local
-  //    position of the tile's slot 0)
+  //    position of the tile's slot 0); a private item's at their global
+  //    positions
   int64_t ndt = 0;
   for (size_t i = 0; i < docs.size(); ++i) {
     const int s = docs[i].first_seg;
+    const int64_t base = seg_is_ctx[s] ? 0 : seg_pos0[s];
     doc_tile_start[i] = (int32_t)ndt;
     const int32_t L = seg_len[s];
     const int32_t nblk = (L + LAZY_BLOCK_SIZE - 1) / LAZY_BLOCK_SIZE;
@@ -365,8 +378,9 @@ extern "C" lazy_status lazy_build_shared_plan(
         return fail(LAZY_ERR_ARG, "segment %d block %d: id %lld outside the pool", s, b, (long long)blk);
       const int32_t valid = (L - LAZY_BLOCK_SIZE * b) < LAZY_BLOCK_SIZE ? (L - LAZY_BLOCK_SIZE * b) : LAZY_BLOCK_SIZE;
       if (ndt >= doc_tiles_cap) return fail(LAZY_ERR_ARG, "doc_tiles_cap %lld too small", (long long)doc_tiles_cap);
-      doc_tiles_out[ndt++] = ((uint64_t)blk << 40) | ((uint64_t)(LAZY_BLOCK_SIZE * b) << 16) |
-                             (uint64_t)((1u << valid) - 1u);
+      const int64_t off = base + (int64_t)LAZY_BLOCK_SIZE * b;
+      if (off > LAZY_MAX_OFFSET) return fail(LAZY_ERR_ARG, "segment %d: offset %lld exceeds 2^24-1", s, (long long)off);
+      doc_tiles_out[ndt++] = ((uint64_t)blk << 40) | ((uint64_t)off << 16) | (uint64_t)((1u << valid) - 1u);
     }
   }
   doc_tile_start[docs.size()] = (int32_t)ndt;
@@ -419,6 +433,14 @@ extern "C" lazy_status lazy_build_shared_plan(
       const bool ctx = seg_is_ctx[s] != 0;
       if (ctx && seen_private) return fail(LAZY_ERR_ARG, "request %d: context segment %d after a private one", r, s);
       if (!ctx) seen_private = true;
+      if (!ctx && private_items && seg_len[s] > 0) {  // the request's private item: one read at Delta 0
+        const int32_t i = doc_of[private_key(s)];
+        if (slot + nchunks[i] > 0xFFFF)
+          return fail(LAZY_ERR_UNSUPPORTED, "request %d needs more than 65535 shared-read slots", r);
+        reads_out[read_start[i] + fill[i]++] = ((uint64_t)r << 48) | ((uint64_t)slot << 32);
+        slot += nchunks[i];
+        continue;
+      }
       if (ctx && seg_len[s] > 0) {
         auto it = doc_of.find(key_of(s));
         if (it != doc_of.end() && it->second >= 0) {

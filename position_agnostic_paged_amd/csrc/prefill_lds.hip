@@ -718,21 +718,11 @@ __device__ __forceinline__ void lds_attend(LdsPrefill<DH, KIND, DEFER, RB, NW, M
         }
       }
 
-      // weights p = 2^(s * scale_log2 - m_run), row sums and P V on the
-      // MFMAs, with the next pair's scores in the same straight-line block
-      // (their products overlap this pair's exponentials); past the last pair
-      // they are computed from a stale buffer and never used
-      F8 pf[RB];
-#pragma unroll
-      for (int b = 0; b < RB; ++b)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pf[b][4 * h + j] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[h][b][j], sl, negm[b]));
       if constexpr (P::kQRot) {
         // a new document from the next pair on: the query rotated for it
-        // before the next pair's scores (its stage and cos/sin row landed
-        // before this iteration's barrier)
+        // before the exponentials, so they, the next pair's scores and the
+        // P V products stay one straight-line block (the next pair's stage
+        // and cos/sin row landed before this iteration's barrier)
         if (dq_next != dq_cur) {
           if (dq_next == 0) {
 #pragma unroll
@@ -745,6 +735,17 @@ __device__ __forceinline__ void lds_attend(LdsPrefill<DH, KIND, DEFER, RB, NW, M
           dq_cur = dq_next;
         }
       }
+      // weights p = 2^(s * scale_log2 - m_run), row sums and P V on the
+      // MFMAs, with the next pair's scores in the same straight-line block
+      // (their products overlap this pair's exponentials); past the last pair
+      // they are computed from a stale buffer and never used
+      F8 pf[RB];
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pf[b][4 * h + j] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[h][b][j], sl, negm[b]));
       pl.scores(pl.stage(p + 1), koff, qr, s);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll

@@ -248,15 +248,15 @@ def build_shared_plan(geom: Geom, kind: int, seg_start, seg_len, seg_pos0, seg_i
     R = ss.shape[0] - 1
     nseg = int(ss[-1])
     cap_tiles = max(1, int(sum((int(n) + 15) // 16 for n in sl)))
-    cap_docs = max(1, int(np.sum(sc)))
+    cap_docs = max(1, int(sl.shape[0]))  # every segment may become an item (min_readers 1: private ones too)
     group = geom.num_q_heads // geom.num_kv_heads
-    # work items: per shared document, (chunks <= tiles/32 + 1) x (row blocks <= readers x G / 16 + 1)
-    per_doc = {}
-    for i in np.flatnonzero(sc):
+    # work items: per item, (chunks <= tiles/32 + 1) x (row blocks <= readers x G / 16 + 1)
+    per_doc = {}  # item -> [tokens, readers]
+    for i in range(sl.shape[0]):
         if sl[i] > 0:
-            k = (int(bl[sb[i]]), int(sl[i]))
-            per_doc[k] = per_doc.get(k, 0) + 1
-    cap_work = 1 + sum(((n + 15) // 16 // 32 + 1) * ((r * group + 15) // 16 + 4) for (_, n), r in per_doc.items())
+            k = (int(bl[sb[i]]), int(sl[i])) if sc[i] else ("private", i)
+            per_doc.setdefault(k, [int(sl[i]), 0])[1] += 1
+    cap_work = 1 + sum(((n + 15) // 16 // 32 + 1) * ((r * group + 15) // 16 + 4) for n, r in per_doc.values())
     out = {"tiles": np.empty(cap_tiles, np.uint64), "tile_start": np.empty(R + 1, np.int32),
            "ctx_tiles": np.empty(max(R, 1), np.int32), "doc_tiles": np.empty(cap_tiles, np.uint64),
            "doc_tile_start": np.empty(cap_docs + 1, np.int32), "read_start": np.empty(cap_docs + 1, np.int32),

@@ -35,24 +35,36 @@ def _batch(rng, num_docs=12, R=7, max_docs=6, dup=True):
 
 def _expected(layouts, kind, num_blocks, group, hkv, rb, min_readers, few):
     """What the plan must contain, derived with plain loops (few: the work-item count under which documents are
-    cut into chunks)."""
-    key = lambda sg: (sg.blocks[0], sg.length)  # noqa: E731
+    cut into chunks).  With min_readers 1 every request's private tokens are one more item, read once at
+    Delta 0 with its tiles at their global positions, and the requests keep no tiles of their own."""
+    key = lambda sg: (sg.blocks[0] << 32) | sg.length  # noqa: E731
     readers = {}
     for lay in layouts:
         for sg in lay.segments:
             if sg.ctx and sg.length > 0:
                 readers[key(sg)] = readers.get(key(sg), 0) + 1
-    first = {}
+    first, nread = {}, {}
+    s_index = 0
     for lay in layouts:
         for sg in lay.segments:
             if sg.ctx and sg.length > 0 and readers[key(sg)] >= min_readers and key(sg) not in first:
                 first[key(sg)] = sg
-    docs = sorted(first, key=lambda k: (-((first[k].length + 15) // 16) * readers[k], (k[0] << 32) | k[1]))
+                nread[key(sg)] = readers[key(sg)]
+            s_index += 1
+    s_index = 0
+    for lay in layouts:
+        for sg in lay.segments:
+            if min_readers == 1 and not sg.ctx and sg.length > 0:
+                k = (1 << 63) | s_index
+                first[k] = sg
+                nread[k] = 1
+            s_index += 1
+    docs = sorted(first, key=lambda k: (-((first[k].length + 15) // 16) * nread[k], k))
     index = {k: i for i, k in enumerate(docs)}
     # chunks: only when the pass holds fewer than `few` work items; then up to ceil(2 few / items) even chunks
     # of at least 32 tiles per document
     ntiles = {k: (first[k].length + 15) // 16 for k in docs}
-    items = hkv * sum(-(-readers[k] * group // (16 * rb)) for k in docs)
+    items = hkv * sum(-(-nread[k] * group // (16 * rb)) for k in docs)
     want = -(-2 * few // items) if 0 < items < few else 1
     ct, nchunks = {}, {}
     for k in docs:
@@ -64,18 +76,22 @@ def _expected(layouts, kind, num_blocks, group, hkv, rb, min_readers, few):
     doc_start = [0]
     for k in docs:
         sg = first[k]
+        base = 0 if sg.ctx else sg.pos0
         for b in range((sg.length + 15) // 16):
             valid = min(16, sg.length - 16 * b)
-            doc_tiles.append((sg.blocks[b] << 40) | ((16 * b) << 16) | ((1 << valid) - 1))
+            doc_tiles.append((sg.blocks[b] << 40) | ((base + 16 * b) << 16) | ((1 << valid) - 1))
         doc_start.append(len(doc_tiles))
     reads = [[] for _ in docs]
     req_reads, own = [], []
+    s_index = 0
     for r, lay in enumerate(layouts):
         slot, keep = 0, []
         for sg in lay.segments:
-            if sg.ctx and sg.length > 0 and key(sg) in index:
-                reads[index[key(sg)]].append((r << 48) | (slot << 32) | sg.pos0)
-                slot += nchunks[key(sg)]
+            k = key(sg) if sg.ctx else (1 << 63) | s_index
+            s_index += 1
+            if sg.length > 0 and k in index:
+                reads[index[k]].append((r << 48) | (slot << 32) | (sg.pos0 if sg.ctx else 0))
+                slot += nchunks[k]
             else:
                 keep.append(sg)
         req_reads.append(slot)
@@ -86,7 +102,7 @@ def _expected(layouts, kind, num_blocks, group, hkv, rb, min_readers, few):
                                         max(1, sum(blocks_for(n) for n in f["seg_len"])))
     work = []
     for i, k in enumerate(docs):
-        n_items = -(-readers[k] * group // (16 * rb))
+        n_items = -(-nread[k] * group // (16 * rb))
         for c in range(nchunks[k]):
             work += [(i, b * rb, c, ct[k]) for b in range(n_items)]
     return {"doc_tiles": doc_tiles, "doc_start": doc_start, "reads": reads, "req_reads": req_reads,
