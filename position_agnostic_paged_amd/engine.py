@@ -384,11 +384,12 @@ class Engine:
 
     def shared_plan(self, layouts: Sequence[RequestLayout], min_readers: int = 1) -> SharedPlan:
         """Plan of a document-major decode: documents read by >= min_readers segments of the batch go through
-        the document pass, the rest through the requests' own tile lists.  By default every cached document
-        goes through the pass (its copies stream whole tile pairs into LDS with the streaming hint), and the
-        split-K pass keeps only the private tokens: on MI355X the mixed 70B step's decode call measured 0.257 ms
-        this way against 0.277 ms with documents read once left to the split-K pass (64 x 32K: 0.226 vs
-        0.248 ms)."""
+        the document pass, the rest through the requests' own tile lists.  By default (min_readers 1) every
+        cached document goes through the pass (its copies stream whole tile pairs into LDS with the streaming
+        hint), and so does each request's private tail, as one more item read once at Delta 0; the split-K
+        pass then has no tiles and is not launched.  On MI355X the mixed 70B step's decode call measured
+        0.277 ms with documents read once left to the split-K pass, 0.257 ms with them in the pass and the
+        private tokens split-K, 0.237 ms with the private tokens in the pass too."""
         return SharedPlan(layouts, self, min_readers)
 
     def decode_shared(self, plan: SharedPlan, q: torch.Tensor, q_pos: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -1,7 +1,7 @@
 """Stream ordering of the document-major decode.
 
-The call's three launches (each request's own tiles, the document pass, the
-combine) go to the caller's stream: its output must be complete once that
+The call's launches (the document pass, the split-K launch over any tiles
+left out of it, the combine) go to the caller's stream: its output must be complete once that
 stream alone is synchronised, on any stream, and repeated calls on
 different streams must give the same bits (the kernels are deterministic:
 no atomics, fixed reduction orders).
