@@ -31,11 +31,14 @@ def logical_sequence(docs: Sequence[Tuple[np.ndarray, np.ndarray]],
                      tail_k: np.ndarray = None, tail_v: np.ndarray = None):
     """Concatenate documents (then an optional tail of private tokens).
 
+    Either part may be empty (a request with no cached document, a decode
+    request with no question): with no document and an empty tail the context
+    is the empty sequence, shaped like the tail.
     Returns raw keys [N][Hkv][dh], values [N][Hkv][dh] and global positions [N].
     """
     ks = [np.asarray(k, np.float64) for k, _ in docs]
     vs = [np.asarray(v, np.float64) for _, v in docs]
-    if tail_k is not None and len(tail_k):
+    if tail_k is not None:
         ks.append(np.asarray(tail_k, np.float64))
         vs.append(np.asarray(tail_v, np.float64))
     k = np.concatenate(ks, axis=0)

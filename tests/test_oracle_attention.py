@@ -181,3 +181,24 @@ def test_decode_matches_prefill_rows():
         vs = np.concatenate([pre_v] + [st[2][None] for st in steps[: s + 1]])
         full = attention.eager_prefill(docs, qs, ks, vs, var)
         assert np.max(np.abs(full[-1] - outs[s])) < 1e-12
+
+
+@pytest.mark.parametrize("kind", ["rope_half", "rope_interleaved", "alibi"])
+def test_decode_without_context_attends_to_itself(kind):
+    """No document and no question: the first generated token sees only itself, so every head's output is
+    that token's value row of its KV head (softmax over one key is 1), whatever the position encoding; the
+    next token mixes the two."""
+    dh, hq, hkv = 16, 4, 2
+    var = _var(kind, dh, hq)
+    empty = np.zeros((0, hkv, dh))
+    steps = [(RNG.standard_normal((hq, dh)), RNG.standard_normal((hkv, dh)), RNG.standard_normal((hkv, dh)))
+             for _ in range(2)]
+    outs = attention.eager_decode([], empty, empty, steps, var)
+    want0 = np.repeat(steps[0][2], hq // hkv, axis=0)
+    assert np.max(np.abs(outs[0] - want0)) < 1e-15
+    # step 1: a convex combination of the two value rows, strictly between them where they differ
+    v0 = np.repeat(steps[0][2], hq // hkv, axis=0)
+    v1 = np.repeat(steps[1][2], hq // hkv, axis=0)
+    lo, hi = np.minimum(v0, v1), np.maximum(v0, v1)
+    assert np.all(outs[1] >= lo - 1e-12) and np.all(outs[1] <= hi + 1e-12)
+    assert np.max(np.abs(outs[1] - v1)) > 1e-6 and np.max(np.abs(outs[1] - v0)) > 1e-6
