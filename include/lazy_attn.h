@@ -278,7 +278,12 @@ lazy_status lazy_attn_decode(const lazy_geom* geom, const lazy_pos_desc* pos, co
  * read among its request's shared reads; Delta = the document's start in
  * that request, < max_pos when max_pos > 0 for RoPE kinds).  Every request
  * keeps a tile list of its unshared documents and private tokens (same
- * layout as lazy_build_tiles).  Work items: (document, first 16-row block,
+ * layout as lazy_build_tiles).  With min_readers 1 no document is unshared,
+ * and each request's private tokens become one more item of the pass as
+ * well: a one-read item whose tiles carry global offsets, read at Delta 0
+ * (query and keys both at global positions; no causal mask is needed in
+ * decode); the request's own tile list is then empty (remaining tiles 0).
+ * Work items: (document, first 16-row block,
  * chunk, tiles per chunk) covering reads x (num_q_heads / num_kv_heads) rows
  * per document, row_blocks x 16 rows each (row_blocks: 8 for bf16, one
  * workgroup of the LDS-staged pass; for fp32 one wave, 2 at dh 128, 4 at
@@ -312,7 +317,8 @@ size_t lazy_attn_decode_shared_workspace_size(const lazy_geom* geom, int32_t num
  * per document serves every request).  Same result as lazy_attn_decode over
  * each request's full tile list, computed in two passes: (1) each request's
  * own tiles (tiles / tile_start / ctx_tiles of the plan: unshared documents
- * and private tokens), split-K as in lazy_attn_decode; (2) every shared
+ * and private tokens), split-K as in lazy_attn_decode, not launched when the
+ * plan leaves none (total_tiles 0, as at min_readers 1); (2) every shared
  * document once per KV head for all its reads together: the query of each
  * read is rotated once by -Delta of that read (RoPE; ALiBi measures the
  * key's distance from q_pos - Delta) against the document's keys at their
