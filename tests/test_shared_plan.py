@@ -169,6 +169,19 @@ def test_plan_refusals():
                             fb["seg_block_start"], fb["blocks"], 8, 0, 2)
 
 
+@pytest.mark.parametrize("min_readers", [1, 2])
+def test_plan_of_an_empty_batch(min_readers):
+    """No request: nothing to read and no work, and the plan still names the geometry's row blocks (the
+    decode call checks them before it returns for an empty batch)."""
+    f = flatten_layouts([])
+    for geom in (L.make_geom(32, 8, 128, "bf16"), L.make_geom(8, 2, 64, "fp32")):
+        h = L.build_shared_plan(geom, 0, f["seg_start"], f["seg_len"], f["seg_pos0"], f["seg_is_ctx"],
+                                f["seg_block_start"], f["blocks"], 16, 0, min_readers)
+        assert (h["num_docs"], h["num_reads"], h["num_work"], h["total_tiles"], h["max_tiles"]) == (0, 0, 0, 0, 0)
+        assert h["row_blocks"] == _pass_shape(geom)[0]
+        assert h["tile_start"].tolist() == [0]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_plan_chunks_few_long_documents(dtype):
     """Three 4096-token documents read by 64 requests: the pass would hold a few dozen (bf16) or a few hundred
